@@ -1,0 +1,345 @@
+"""Benchmark of shared-prompt tree attention, forward + backward, on one GPU.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole path over one batch of synthetic replay
+trees: prompt prefill, response replay forward, replay backward (prompt
+seeds summed over every branch) and prefill backward.  Inputs are resident
+in HBM before the timed region.  The metric is useful tree-masked TFLOP/s:
+14 * head_dim FLOPs (4d forward, 10d backward) per valid (query row, key)
+pair and query head, divided by the step time.
+
+Prints one JSON line.  Besides the headline numbers it carries:
+  breakdown_ms       time per entry point (HIP events between the calls)
+  roofline           the dominant kernel's own duration (HIP events recorded
+                     by the library around that kernel) against the bf16
+                     MFMA peak
+  flattened_baseline the same attention computed the way flattened context
+                     parallelism does it: every (prompt, response) pair as
+                     its own causal sequence, with the same kernels
+  cpu_baseline       the float64 oracle on a bounded sample, host cores
+  also               the same measurement for a second workload
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12  # 256 CUs x 2.4 GHz x 4096 flop/clk/CU
+HBM_GBPS = 8000.0
+
+# Algorithmic FLOPs per valid pair and query head, per head_dim, of each
+# main kernel: forward S and PV; dQ kernel recomputes S and dP and forms dQ;
+# dK/dV kernel recomputes S and dP and forms dV and dK.
+KERNEL_FLOPS_PER_PAIR_DIM = {"fwd": 4, "dq": 6, "dkv": 8}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="prompt_heavy")
+    p.add_argument("--also", default="response_heavy",
+                   help="second workload measured the same way ('none' to skip)")
+    p.add_argument("--no-flattened", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-workers", type=int, default=0)
+    p.add_argument("--copy-calibration-mib", type=int, default=1024,
+                   help="size of a plain device copy run after the timed region, used to "
+                        "scale HBM byte counters in profiling runs (0 to skip)")
+    return p.parse_args()
+
+
+def fail(msg):
+    print(msg, file=sys.stderr, flush=True)
+    sys.exit(2)
+
+
+def measure_workload(name, steps, warmup, flattened=True):
+    import torch
+
+    from shared_prompt_tree_amd import ops
+    from shared_prompt_tree_amd import workloads as wl
+
+    spec = wl.SPECS[name]
+    tree = wl.make_tree(spec)
+    dev = torch.device("cuda:0")
+    t = wl.make_tensors(tree, spec.seed, device=dev, value_scale=spec.value_scale)
+    prob = ops.TreeProblem.from_tree(tree, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        return ops.tree_attention_forward_backward(prob, t)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # whole steps
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record()
+    for _ in range(steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - w0) * 1e3 / steps
+    ms = ev0.elapsed_time(ev1) / steps
+
+    # per entry point, and every main kernel's own duration
+    names = ["prefill", "replay_fwd", "replay_bwd", "prefill_bwd"]
+    part = {n: 0.0 for n in names}
+    kern = {k: 0.0 for k in ("fwd", "dq", "dkv")}
+    kinds = {"fwd": ops.KERNEL_FWD, "dq": ops.KERNEL_DQ, "dkv": ops.KERNEL_DKV}
+
+    def new_event():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    for _ in range(steps):
+        evs = [new_event() for _ in range(5)]
+        # kernel events: fwd in prefill and replay_fwd, dq and dkv in both bwd calls
+        kev = {(k, c): (new_event(), new_event()) for k in kern for c in range(2)}
+        torch.cuda.synchronize()
+        evs[0].record()
+        ops.tree_attn_set_kernel_events(kinds["fwd"], *kev[("fwd", 0)])
+        o_p, lse_p = ops.tree_attn_prefill(prob, t["q_p"], t["k_p"], t["v_p"])
+        evs[1].record()
+        ops.tree_attn_set_kernel_events(kinds["fwd"], *kev[("fwd", 1)])
+        o_r, lse_r = ops.tree_attn_replay_fwd(prob, t["k_p"], t["v_p"], t["q_r"], t["k_r"],
+                                              t["v_r"])
+        evs[2].record()
+        ops.tree_attn_set_kernel_events(kinds["dq"], *kev[("dq", 0)])
+        ops.tree_attn_set_kernel_events(kinds["dkv"], *kev[("dkv", 0)])
+        dq_r, dk_r, dv_r, dks, dvs = ops.tree_attn_replay_bwd(
+            prob, t["k_p"], t["v_p"], t["q_r"], t["k_r"], t["v_r"], o_r, lse_r, t["do_r"])
+        evs[3].record()
+        ops.tree_attn_set_kernel_events(kinds["dq"], *kev[("dq", 1)])
+        ops.tree_attn_set_kernel_events(kinds["dkv"], *kev[("dkv", 1)])
+        ops.tree_attn_prefill_bwd(prob, t["q_p"], t["k_p"], t["v_p"], o_p, lse_p, t["do_p"],
+                                  dks, dvs)
+        evs[4].record()
+        for k in kinds.values():
+            ops.tree_attn_set_kernel_events(k)
+        torch.cuda.synchronize()
+        for i, n in enumerate(names):
+            part[n] += evs[i].elapsed_time(evs[i + 1]) / steps
+        for (k, c), (a, b) in kev.items():
+            kern[k] += a.elapsed_time(b) / steps
+    per_call = {}  # the biggest single launch of each kernel kind
+
+    pairs = wl.pair_counts(tree)
+    useful = wl.useful_flops(tree)
+    hq, d = tree.hq, tree.d
+    rep = {
+        "ms_per_step": ms,
+        "wall_ms_per_step": wall_ms,
+        "useful_tflop_per_step": useful / 1e12,
+        "tflops": useful / (ms * 1e-3) / 1e12,
+        "breakdown_ms": {k: round(v, 4) for k, v in part.items()},
+        "kernel_ms": {k: round(v, 4) for k, v in kern.items()},
+    }
+    # algorithmic FLOPs of each kernel kind over one step
+    kflops = {k: pairs["tree"] * hq * d * f for k, f in KERNEL_FLOPS_PER_PAIR_DIM.items()}
+    dom = max(kern, key=kern.get)
+    achieved = kflops[dom] / (kern[dom] * 1e-3) / 1e12
+    rep["roofline"] = {
+        "kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
+        "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+        "flops_per_pair_per_dim": KERNEL_FLOPS_PER_PAIR_DIM[dom],
+        "launches_per_step": 2, "ms_per_step": round(kern[dom], 4),
+    }
+    rep["kernel_tflops"] = {k: round(kflops[k] / (kern[k] * 1e-3) / 1e12, 2) for k in kern}
+    del per_call
+
+    if flattened:
+        ftree = wl.flattened_tree(tree)
+        ft = wl.flatten_tensors(tree, t)
+        fprob = ops.TreeProblem.from_tree(ftree, device=dev)
+
+        def fstep():
+            o, l = ops.tree_attn_prefill(fprob, ft["q_p"], ft["k_p"], ft["v_p"])
+            ops.tree_attn_prefill_bwd(fprob, ft["q_p"], ft["k_p"], ft["v_p"], o, l, ft["do_p"])
+
+        fstep()
+        torch.cuda.synchronize()
+        fsteps = max(1, min(steps, 5))
+        ev0.record()
+        for _ in range(fsteps):
+            fstep()
+        ev1.record()
+        torch.cuda.synchronize()
+        fms = ev0.elapsed_time(ev1) / fsteps
+        rep["flattened_baseline"] = {
+            "ms_per_step": round(fms, 3),
+            "useful_tflops": round(useful / (fms * 1e-3) / 1e12, 2),
+            "work_ratio": round(pairs["flattened"] / pairs["tree"], 3),
+            "speedup_of_tree": round(fms / ms, 3),
+            "note": "same kernels over one causal sequence per (prompt, response) pair; "
+                    "same tree-masked numerator",
+        }
+        del ft
+    rep["config"] = {
+        "workload": name, "groups": tree.n_groups, "q_heads": tree.hq, "kv_heads": tree.hkv,
+        "head_dim": tree.d, "prompt_len": spec.prompt_len, "branches_per_group": spec.g,
+        "resp_len": list(spec.resp), "prompt_tokens": tree.prompt_tokens,
+        "response_tokens": tree.resp_tokens, "seed": spec.seed,
+        "valid_pairs_per_head": pairs["tree"],
+    }
+    rep["_tree"] = tree
+    rep["_tensors"] = t
+    return rep
+
+
+def cpu_baseline(tree, t, workers):
+    """The float64 oracle on a bounded sample of the workload: for one query
+    head per worker, the flattened (prompt, first branch) sequence of group 0,
+    evaluated on its last 8192 prompt rows and its first 512 response rows
+    (the whole key range each), in a process pool."""
+    import multiprocessing as mp
+
+    import numpy as np
+    import torch
+
+    import oracle  # the oracle is only used for this baseline
+
+    g, i = 0, int(tree.group_branch_cu[0])
+    P = int(tree.prompt_cu[1])
+    r0, r1 = int(tree.resp_cu[i]), int(tree.resp_cu[i + 1])
+    n_resp = min(512, r1 - r0)
+    rows = np.concatenate([np.arange(max(0, P - 8192), P), np.arange(P, P + n_resp)])
+    heads = list(range(min(workers, tree.hq)))
+    seqs = []
+    for h in heads:
+        kv = h * tree.hkv // tree.hq
+
+        def cat(a, b, hh):
+            return torch.cat([t[a][:P, hh], t[b][r0:r1, hh]]).to("cpu", torch.float64).numpy()
+
+        seqs.append((cat("q_p", "q_r", h), cat("k_p", "k_r", kv), cat("v_p", "v_r", kv),
+                     cat("do_p", "do_r", h)))
+    scale = 1.0 / math.sqrt(tree.d)
+    global _CPU_SEQS, _CPU_ROWS, _CPU_SCALE
+    _CPU_SEQS, _CPU_ROWS, _CPU_SCALE = seqs, rows, scale
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(len(heads)) as pool:
+        pool.map(_cpu_unit, range(len(heads)))
+    dt = time.perf_counter() - t0
+    pairs = int(sum(int(r) + 1 for r in rows)) * len(heads)
+    flops = pairs * tree.d * 14
+    return {
+        "value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": len(heads),
+        "kind": "oracle", "seconds": round(dt, 2),
+        "sample": f"{len(heads)} query heads x {len(rows)} rows (last {P - int(rows[0])} "
+                  f"prompt rows, first {n_resp} response rows of branch 0, group 0) of the "
+                  f"flattened sequence, full key range per row, forward+backward, float64",
+    }
+
+
+_CPU_SEQS = _CPU_ROWS = _CPU_SCALE = None
+
+
+def _cpu_unit(k):
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    q, kk, v, do = _CPU_SEQS[k]
+    with threadpool_limits(1):
+        oracle.causal_unit(q, kk, v, do, _CPU_SCALE, rows=_CPU_ROWS)
+    return k
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        fail("bench.py measures one GPU: this build has no multi-GPU path "
+             "(every box has one GPU); run with --gpus 1")
+    import torch
+
+    if not torch.cuda.is_available():
+        fail("no GPU visible")
+    from shared_prompt_tree_amd import ops
+
+    ops.library()  # fail loudly if the HIP library is missing
+    print(f"[bench] workload {args.workload}: warmup {args.warmup}, steps {args.steps}",
+          file=sys.stderr, flush=True)
+    main_rep = measure_workload(args.workload, args.steps, args.warmup, not args.no_flattened)
+    print(f"[bench] {args.workload}: {main_rep['ms_per_step']:.2f} ms/step, "
+          f"{main_rep['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    cpu = None
+    if not args.no_cpu_baseline:
+        workers = args.cpu_workers or min(16, os.cpu_count() or 1)
+        cpu = cpu_baseline(main_rep["_tree"], main_rep["_tensors"], workers)
+        print(f"[bench] cpu baseline {cpu['value']} TFLOP/s in {cpu['seconds']} s",
+              file=sys.stderr, flush=True)
+    main_rep.pop("_tree")
+    main_rep.pop("_tensors")
+    torch.cuda.empty_cache()
+    also = None
+    if args.also and args.also != "none" and args.also != args.workload:
+        print(f"[bench] workload {args.also}", file=sys.stderr, flush=True)
+        a = measure_workload(args.also, args.steps, args.warmup, not args.no_flattened)
+        a.pop("_tree")
+        a.pop("_tensors")
+        also = {
+            "workload": args.also, "value": round(a["tflops"], 2), "unit": "TFLOP/s",
+            "ms_per_step": round(a["ms_per_step"], 3),
+            "pct_of_bf16_peak": round(100 * a["tflops"] / PEAK_BF16_TFLOPS, 2),
+            "breakdown_ms": a["breakdown_ms"], "kernel_ms": a["kernel_ms"],
+            "kernel_tflops": a["kernel_tflops"], "roofline": a["roofline"],
+            "flattened_baseline": a.get("flattened_baseline"), "config": a["config"],
+        }
+        print(f"[bench] {args.also}: {a['ms_per_step']:.2f} ms/step, {a['tflops']:.1f} TFLOP/s",
+              file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+    if args.copy_calibration_mib > 0:
+        # A plain copy of known size, outside the timed region: profiling runs
+        # scale the HBM byte counters of the kernels above by what the same
+        # counters read for this kernel.
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    line = {
+        "metric": "tree-attention fwd+bwd useful TFLOP/s per GPU",
+        "value": round(main_rep["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_rep["ms_per_step"], 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "pct_of_bf16_peak": round(100 * main_rep["tflops"] / PEAK_BF16_TFLOPS, 2),
+        "config": main_rep["config"],
+        "useful_tflop_per_step": round(main_rep["useful_tflop_per_step"], 3),
+        "wall_ms_per_step": round(main_rep["wall_ms_per_step"], 3),
+        "breakdown_ms": main_rep["breakdown_ms"],
+        "kernel_ms": main_rep["kernel_ms"],
+        "kernel_tflops": main_rep["kernel_tflops"],
+        "roofline": main_rep["roofline"],
+        "flattened_baseline": main_rep.get("flattened_baseline"),
+        "cpu_baseline": cpu,
+        "also": also,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

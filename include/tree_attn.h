@@ -1,0 +1,218 @@
+/*
+ * tree_attn.h -- C ABI of libtreeattn.so: shared-prompt tree attention on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Method: "Splitting Prompt Prefill from Response Replay for Context-Parallel
+ * Long-Context LLM Post-Training" (the AugTree paper).  A replay tree is one
+ * shared prompt P and G response branches R_1..R_G (section 3.1).  The prompt
+ * is prefilled once with causal attention and its K/V kept (section 3.2,
+ * "Shared prompt prefill pass"); every response token then attends to the
+ * whole prompt and to its own branch prefix, never to a sibling (section 3.2,
+ * Eq. 1).  Prompt K/V gradients are the sum over all branches (section 3.2,
+ * Eq. 2) and flow back through the prefill (section 3.2, "Exact many-to-one
+ * backward").  Attention per head is O = softmax(Q K^T * scale + M) V
+ * (section 2.2).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout.  Tensors are packed token-major and contiguous:
+ *   prompt   Q/O/dQ/dO [sum_g P_g, Hq, d],   K/V/dK/dV [sum_g P_g, Hkv, d]
+ *   response Q/O/dQ/dO [sum_i r_i,  Hq, d],  K/V/dK/dV [sum_i r_i,  Hkv, d]
+ *   LSE [Hq, tokens] float32: natural log of sum_j exp(scale * q . k_j)
+ *   over the visible keys of that row.
+ * Branches of one group are consecutive in the response tensors.  Query
+ * head h reads kv head floor(h * Hkv / Hq).  The causal masks include the
+ * diagonal.
+ * dtype.  TREE_ATTN_BF16 or TREE_ATTN_F32 for every I/O tensor; LSE, prompt
+ * gradient seeds and merge partials are always float32.  Matrix products
+ * accumulate in float32.
+ * Memory.  Every tensor pointer is caller-owned device memory with a
+ * 16-byte aligned base.  The library allocates no device memory.  Scratch
+ * space comes from the caller through (ws, ws_bytes), sized by
+ * tree_attn_workspace_size(); its contents need not be preserved between
+ * calls.  Host arrays (*_h) are read during the call only; device arrays
+ * (*_d) and every tensor must stay valid until the enqueued work finishes.
+ * The *_h and *_d copies of an offset array must hold the same values.
+ * Streams.  Each call only enqueues work on `stream` (a hipStream_t; NULL is
+ * the default stream) and never synchronises.  Calls that share workspace
+ * must be ordered on one stream.
+ * Errors.  0 on success, else a negative tree_attn_status.  Arguments are
+ * checked on the host before any HIP call, so a rejected call enqueues
+ * nothing and writes nothing.  TREE_ATTN_ERR_HIP reports a failed launch.
+ * The library holds no global mutable state apart from the per-thread
+ * timing hook below, and may be called from several host threads.
+ */
+#ifndef TREE_ATTN_H_
+#define TREE_ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* tree_attn_stream_t; /* a hipStream_t */
+
+typedef enum {
+  TREE_ATTN_F32 = 0,
+  TREE_ATTN_BF16 = 1
+} tree_attn_dtype;
+
+typedef enum {
+  TREE_ATTN_OK = 0,
+  TREE_ATTN_ERR_INVALID = -1,     /* null pointer, bad offsets, bad shape */
+  TREE_ATTN_ERR_UNSUPPORTED = -2, /* dtype or head_dim not supported */
+  TREE_ATTN_ERR_WORKSPACE = -3,   /* ws_bytes below the required size */
+  TREE_ATTN_ERR_HIP = -4          /* a HIP launch or runtime call failed */
+} tree_attn_status;
+
+typedef enum {
+  TREE_ATTN_OP_PREFILL = 0,
+  TREE_ATTN_OP_REPLAY_FWD = 1,
+  TREE_ATTN_OP_REPLAY_BWD = 2,
+  TREE_ATTN_OP_PREFILL_BWD = 3
+} tree_attn_op;
+
+/*
+ * A batch of replay trees T = (P, {R_i}) (section 3.1).
+ * num_groups    n_g >= 1 prompts.
+ * num_branches  total branches over all groups (>= 0).
+ * num_q_heads, num_kv_heads  Hq, Hkv >= 1 with Hq % Hkv == 0.
+ * head_dim      64 or 128.
+ * dtype         a tree_attn_dtype.
+ * softmax_scale the score scale; 1/sqrt(head_dim) is the paper's choice.
+ * prompt_cu     [n_g + 1] non-decreasing token offsets of each prompt in the
+ *               prompt tensors, prompt_cu[0] == 0 (P_g >= 0).
+ * group_branch_cu [n_g + 1] non-decreasing, group g owns branches
+ *               group_branch_cu[g] .. group_branch_cu[g+1]-1;
+ *               group_branch_cu[0] == 0, group_branch_cu[n_g] == num_branches.
+ * resp_cu       [num_branches + 1] non-decreasing token offsets of each
+ *               branch in the response tensors, resp_cu[0] == 0 (r_i >= 0).
+ * Each offset array is given twice: *_h in host memory, *_d in device
+ * memory, with equal contents.  The device copies may be NULL only for an
+ * entry point that does not read them (none of the four attention calls).
+ */
+typedef struct {
+  int32_t num_groups;
+  int32_t num_branches;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t dtype;
+  float softmax_scale;
+  const int32_t* prompt_cu_h;
+  const int32_t* prompt_cu_d;
+  const int32_t* group_branch_cu_h;
+  const int32_t* group_branch_cu_d;
+  const int32_t* resp_cu_h;
+  const int32_t* resp_cu_d;
+} tree_attn_problem;
+
+/*
+ * Bytes of workspace that entry point `op` (a tree_attn_op) needs for this
+ * problem.  Writes *bytes; no HIP call.
+ */
+int tree_attn_workspace_size(const tree_attn_problem* problem, int op, size_t* bytes);
+
+/*
+ * Prompt prefill (section 3.2, "Shared prompt prefill pass"): causal
+ * attention of each group's prompt over its own prompt, computed once per
+ * group.
+ *   in : q_p [sum P, Hq, d], k_p, v_p [sum P, Hkv, d]
+ *   out: o_p [sum P, Hq, d], lse_p [Hq, sum P] (float32)
+ * The caller keeps k_p / v_p as the prompt K/V state for replay.
+ */
+int tree_attn_prefill(const tree_attn_problem* problem, const void* q_p, const void* k_p,
+                      const void* v_p, void* o_p, float* lse_p, void* ws, size_t ws_bytes,
+                      tree_attn_stream_t stream);
+
+/*
+ * Response replay forward (section 3.2, "Response replay"; Eq. 1): row t of
+ * branch i attends to every key of its group's prompt (no mask) and to keys
+ * 0..t of branch i (causal).  Both parts share one online-softmax state per
+ * row, which is the partial-state merge of section 3.3 done in registers.
+ *   in : k_p, v_p [sum P, Hkv, d] (prompt K/V state from prefill),
+ *        q_r [sum r, Hq, d], k_r, v_r [sum r, Hkv, d]
+ *   out: o_r [sum r, Hq, d], lse_r [Hq, sum r] (float32)
+ */
+int tree_attn_replay_fwd(const tree_attn_problem* problem, const void* k_p, const void* v_p,
+                         const void* q_r, const void* k_r, const void* v_r, void* o_r,
+                         float* lse_r, void* ws, size_t ws_bytes, tree_attn_stream_t stream);
+
+/*
+ * Response replay backward (section 3.2, Eq. 2).  Given the replay forward's
+ * o_r, lse_r and the upstream gradient do_r:
+ *   out: dq_r [sum r, Hq, d], dk_r, dv_r [sum r, Hkv, d] (I/O dtype), and
+ *        dk_p_seed, dv_p_seed [sum P, Hkv, d] float32: the response rows'
+ *        gradient on the prompt K/V, summed over every branch of the group
+ *        and over the query heads of each kv head.  The seeds are
+ *        overwritten, not accumulated.  Passing NULL for both skips them
+ *        (a detached prompt); passing exactly one NULL is invalid.
+ */
+int tree_attn_replay_bwd(const tree_attn_problem* problem, const void* k_p, const void* v_p,
+                         const void* q_r, const void* k_r, const void* v_r, const void* o_r,
+                         const float* lse_r, const void* do_r, void* dq_r, void* dk_r,
+                         void* dv_r, float* dk_p_seed, float* dv_p_seed, void* ws,
+                         size_t ws_bytes, tree_attn_stream_t stream);
+
+/*
+ * Prompt prefill backward (section 3.2: prompt-state gradient seeds are
+ * propagated through the original prefill).  Causal backward of the prompt
+ * over itself, plus the seeds:
+ *   dk_p = prefill term + dk_p_seed,  dv_p = prefill term + dv_p_seed,
+ *   dq_p = prefill term.
+ *   in : q_p, k_p, v_p, o_p, lse_p (from tree_attn_prefill), do_p,
+ *        dk_p_seed, dv_p_seed float32 (from tree_attn_replay_bwd; both NULL
+ *        means zero seeds; exactly one NULL is invalid)
+ *   out: dq_p [sum P, Hq, d], dk_p, dv_p [sum P, Hkv, d] (I/O dtype)
+ */
+int tree_attn_prefill_bwd(const tree_attn_problem* problem, const void* q_p, const void* k_p,
+                          const void* v_p, const void* o_p, const float* lse_p,
+                          const void* do_p, const float* dk_p_seed, const float* dv_p_seed,
+                          void* dq_p, void* dk_p, void* dv_p, void* ws, size_t ws_bytes,
+                          tree_attn_stream_t stream);
+
+/*
+ * Merge of partial attention states for the same query rows (section 3.3,
+ * MoveQ, and Fig. 8: partial online-softmax states (m, l, O_acc) are merged
+ * associatively, not normalised outputs).  A part is (O_k, LSE_k) with O_k
+ * normalised; O_acc = l O and m = LSE - ln l carry the same information.
+ *   LSE = ln sum_k exp(LSE_k),  O = sum_k exp(LSE_k - LSE) O_k.
+ * A part with LSE_k = -inf (no visible key) is the identity; if every part
+ * is empty the row gets LSE = -inf and O = 0.
+ *   in : o_parts [num_splits, rows, heads, head_dim] float32,
+ *        lse_parts [num_splits, heads, rows] float32
+ *   out: o_out [rows, heads, head_dim] in out_dtype (a tree_attn_dtype),
+ *        lse_out [heads, rows] float32
+ * num_splits >= 1, rows >= 0, heads >= 1, head_dim in {64, 128}.
+ */
+int lse_merge(int32_t num_splits, int32_t rows, int32_t heads, int32_t head_dim,
+              int32_t out_dtype, const float* o_parts, const float* lse_parts, void* o_out,
+              float* lse_out, tree_attn_stream_t stream);
+
+/* A static description of a tree_attn_status code. */
+const char* tree_attn_error_string(int code);
+
+/*
+ * Kernel timing hook for benchmarks and profilers.  kind 0 is the forward
+ * attention kernel, 1 the dQ kernel, 2 the dK/dV kernel.  While set, every
+ * launch of that kernel from the calling host thread records start_event
+ * (a hipEvent_t) on the launch stream just before the kernel and
+ * stop_event just after it; a later launch records them again.  NULL for
+ * both events clears the hook.  Returns TREE_ATTN_ERR_INVALID for an
+ * unknown kind or exactly one NULL event.  No HIP call.
+ */
+int tree_attn_set_kernel_events(int kind, void* start_event, void* stop_event);
+
+/*
+ * The hipError_t value behind the last TREE_ATTN_ERR_HIP returned on the
+ * calling host thread (0 if none).  No HIP call.
+ */
+int tree_attn_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TREE_ATTN_H_ */

@@ -1,0 +1,621 @@
+// Attention backward for gfx950 (AugTree paper, section 3.2, "Exact
+// many-to-one backward", Eq. 2).
+//
+// With P = exp(scale * Q K^T - LSE), D = rowsum(dO * O), dP = dO V^T and
+// dS = P * (dP - D):  dQ = scale * dS K,  dK = scale * dS^T Q,  dV = P^T dO.
+//
+// dkv_kernel is key-stationary.  A workgroup (4 waves x 32 keys) owns 128 keys
+// of one kv head, keeps their K and V in registers, and loops over every
+// query row that reads them, for all query heads of that kv head.  For a
+// prompt tile in replay that is every response row of every branch of the
+// group, so the sum over branches of Eq. 2 happens in the accumulators and
+// the float32 seeds are written once, without atomics.  Query rows stream
+// through LDS in blocks of 32, double buffered; Q^T and dO^T come from
+// pre-transposed copies so that every operand is read with 16-byte LDS
+// loads.
+//
+// dq_kernel is query-stationary, tiled like the forward kernel: 8 waves x 32
+// query rows, keys streamed in tiles of 64 from segment A (no mask) and then
+// segment B (causal).  It recomputes P and dP per tile and accumulates
+// dQ^T += K^T dS^T with K^T read from a pre-transposed copy.
+#include <hip/hip_ext.h>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace treeattn {
+
+// ------------------------------------------------------------------ dQ
+
+template <typename T, int D>
+struct DqArgs {
+  const T* q;
+  const T* dout;
+  const float* lse;
+  const float* delta;
+  T* dq;
+  const T* k_a;
+  const T* v_a;
+  const T* kt_a;
+  const T* k_b;
+  const T* v_b;
+  const T* kt_b;
+  const QItem* items;
+  int n_items;
+  int hq, hkv, hp, n_hg;
+  int lse_stride;
+  int kt_a_stride, kt_b_stride;
+  float scale_log2, scale;
+};
+
+// KB 32-key blocks per step: 2 (64 keys), or 1 where two double-buffered
+// stages of K, V and K^T would not fit in LDS (float32 at head_dim 128).
+template <typename T, int D, int KB>
+__global__ __launch_bounds__(512) void dq_kernel(DqArgs<T, D> a) {
+  constexpr int NT = 512, KT = 32 * KB, CH = ChunkOf<T>::kElems;
+  constexpr int NCHK = D / CH, NCHT = KT / CH;
+  constexpr int KTILE = KT * D;
+  constexpr int KCH = KT * NCHK, TCH = D * NCHT;
+  constexpr int KPER = (KCH + NT - 1) / NT, TPER = (TCH + NT - 1) / NT;
+  constexpr int NKK = D / 16, NDB = D / 32;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  T* smem = reinterpret_cast<T*>(smem_raw);
+
+  int item_idx, hg;
+  if (!xcd_map(blockIdx.x, a.n_items, a.n_hg, item_idx, hg)) return;
+  const QItem it = a.items[item_idx];
+  if (it.nq <= 0) return;
+  const int kv = (hg * a.hp) / (a.hq / a.hkv);
+
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int lr = l & 31, lh = l >> 5;
+  const int row = 32 * w + lr;
+  const int tok = row / a.hp;
+  const int head = hg * a.hp + (row % a.hp);
+  const bool qvalid = tok < it.nq;
+
+  Frag<T> qf[NKK], gf[NKK];
+  float lse2 = INFINITY, dl = 0.f;
+  {
+    const size_t off = ((size_t)(it.q0 + (qvalid ? tok : 0)) * a.hq + head) * D;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      if (qvalid) {
+        load_frag(qf[kk], a.q + off + 16 * kk + 8 * lh);
+        load_frag(gf[kk], a.dout + off + 16 * kk + 8 * lh);
+      } else {
+        qf[kk].v = {};
+        gf[kk].v = {};
+      }
+    }
+    if (qvalid) {
+      const size_t li = (size_t)head * a.lse_stride + it.q0 + tok;
+      lse2 = a.lse[li] * kLog2e;
+      dl = a.delta[li];
+    }
+  }
+
+  const int na = (it.alen + KT - 1) / KT;
+  const int nb = (it.blen + KT - 1) / KT;
+  const int total = na + nb;
+  const size_t kv_stride = (size_t)a.hkv * D;
+
+  u32x4 kst[KPER], vst[KPER], tst[TPER];
+  auto gload = [&](int j) {
+    const bool inA = j < na;
+    const int ks = (inA ? j : j - na) * KT;
+    const size_t base = (size_t)(inA ? it.a0 : it.b0) * kv_stride;
+    const T* kb = (inA ? a.k_a : a.k_b) + base;
+    const T* vb = (inA ? a.v_a : a.v_b) + base;
+    const int klen = inA ? it.alen : it.blen;
+#pragma unroll
+    for (int i = 0; i < KPER; ++i) {
+      const int qi = tid + NT * i;
+      if (KCH % NT == 0 || qi < KCH) {
+        const int r = qi / NCHK, c = qi % NCHK;
+        const int key = ks + r;
+        if (key < klen) {
+          const size_t o = (size_t)key * kv_stride + kv * D + c * CH;
+          kst[i] = *reinterpret_cast<const u32x4*>(kb + o);
+          vst[i] = *reinterpret_cast<const u32x4*>(vb + o);
+        } else {
+          kst[i] = u32x4{0, 0, 0, 0};
+          vst[i] = u32x4{0, 0, 0, 0};
+        }
+      }
+    }
+    const int tstride = inA ? a.kt_a_stride : a.kt_b_stride;
+    const T* tb = (inA ? a.kt_a + (size_t)kv * D * a.kt_a_stride + it.apad
+                       : a.kt_b + (size_t)kv * D * a.kt_b_stride + it.bpad) + ks;
+#pragma unroll
+    for (int i = 0; i < TPER; ++i) {
+      const int qi = tid + NT * i;
+      if (TCH % NT == 0 || qi < TCH) {
+        const int dd = qi / NCHT, c = qi % NCHT;
+        tst[i] = *reinterpret_cast<const u32x4*>(tb + (size_t)dd * tstride + c * CH);
+      }
+    }
+  };
+  auto lstore = [&](int stage) {
+    T* ks_ = smem + stage * 3 * KTILE;
+    T* vs_ = ks_ + KTILE;
+    T* ts_ = vs_ + KTILE;
+#pragma unroll
+    for (int i = 0; i < KPER; ++i) {
+      const int qi = tid + NT * i;
+      if (KCH % NT == 0 || qi < KCH) {
+        const int r = qi / NCHK, c = qi % NCHK;
+        const int o = r * D + ((c ^ swz_row<NCHK>(r)) * CH);
+        *reinterpret_cast<u32x4*>(ks_ + o) = kst[i];
+        *reinterpret_cast<u32x4*>(vs_ + o) = vst[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < TPER; ++i) {
+      const int qi = tid + NT * i;
+      if (TCH % NT == 0 || qi < TCH) {
+        const int dd = qi / NCHT, c = qi % NCHT;
+        *reinterpret_cast<u32x4*>(ts_ + dd * KT + ((c ^ swz_row<NCHT>(dd)) * CH)) = tst[i];
+      }
+    }
+  };
+
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+  const float c2 = a.scale_log2;
+  const int wave_tok0 = (32 * w) / a.hp;
+
+  if (total > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
+  for (int j = 0; j < total; ++j) {
+    if (j + 1 < total) gload(j + 1);
+    const T* ks_ = smem + (j & 1) * 3 * KTILE;
+    const T* vs_ = ks_ + KTILE;
+    const T* ts_ = vs_ + KTILE;
+
+    f32x16 s[KB], dp[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      s[kb] = f32x16{};
+      dp[kb] = f32x16{};
+      const int kr = 32 * kb + lr;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        Frag<T> kf, vf;
+        lds_frag(kf, ks_, kr, D, 16 * kk + 8 * lh, swz_row<NCHK>(kr));
+        lds_frag(vf, vs_, kr, D, 16 * kk + 8 * lh, swz_row<NCHK>(kr));
+        mma(s[kb], kf, qf[kk]);
+        mma(dp[kb], vf, gf[kk]);
+      }
+    }
+    const bool inA = j < na;
+    const int kst0 = (inA ? j : j - na) * KT;
+    const bool need_mask = inA ? (kst0 + KT > it.alen) : (kst0 + KT - 1 > it.qpos + wave_tok0);
+    const int lim = inA ? it.alen - 1 : it.qpos + tok;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) {
+        float p = fast_exp2(s[kb][jj] * c2 - lse2);
+        if (need_mask) {
+          const int key = kst0 + 32 * kb + 8 * (jj >> 2) + 4 * lh + (jj & 3);
+          if (key > lim) p = 0.f;
+        }
+        s[kb][jj] = p * (dp[kb][jj] - dl);
+      }
+    Frag<T> sf[KB][2];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) to_frag(sf[kb][hf], s[kb], 8 * hf);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int tr = 32 * db + lr;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          Frag<T> tf;
+          lds_frag(tf, ts_, tr, KT, 16 * (2 * kb + hf) + 8 * lh, swz_row<NCHT>(tr));
+          mma(acc[db], tf, sf[kb][hf]);
+        }
+    }
+    if (j + 1 < total) lstore((j + 1) & 1);
+    __syncthreads();
+  }
+
+  if (!qvalid) return;
+  T* drow = a.dq + ((size_t)(it.q0 + tok) * a.hq + head) * D;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d0 = 32 * db + 8 * g4 + 4 * lh;
+      if constexpr (sizeof(T) == 2) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = static_cast<bf16>(acc[db][4 * g4 + e] * a.scale);
+        *reinterpret_cast<bf16x4*>(drow + d0) = v;
+      } else {
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[db][4 * g4 + e] * a.scale;
+        *reinterpret_cast<f32x4*>(drow + d0) = v;
+      }
+    }
+}
+
+// ------------------------------------------------------------------ dK dV
+
+template <typename T, int D>
+struct DkvArgs {
+  const T* k;
+  const T* v;
+  const T* k_prompt;
+  const T* v_prompt;
+  const T* q;
+  const T* dout;
+  const T* qt;
+  const T* dot;
+  const float* lse;
+  const float* delta;
+  const int32_t* seg_cu;
+  const int32_t* seg_pad;
+  T* dk;
+  T* dv;
+  float* dk_seed;
+  float* dv_seed;
+  const KItem* items;
+  int n_items;
+  int hq, hkv, hp, nsub;
+  int lse_stride, qt_stride;
+  float scale_log2, scale;
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void dkv_kernel(DkvArgs<T, D> a) {
+  constexpr int NT = 256, QB = 32, CH = ChunkOf<T>::kElems;
+  constexpr int NCHQ = D / CH, NCHT = QB / CH;
+  constexpr int QTILE = QB * D;                   // elements per staged tensor
+  constexpr int STAGE = 4 * QTILE;                // Q, dO, Q^T, dO^T
+  constexpr int QCH = QB * NCHQ, TCH = D * NCHT;  // chunks per tensor
+  constexpr int QPER = (QCH + NT - 1) / NT, TPER = (TCH + NT - 1) / NT;
+  constexpr int NKK = D / 16, NDB = D / 32;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  T* smem = reinterpret_cast<T*>(smem_raw);
+  float* fsm = reinterpret_cast<float*>(smem + 2 * STAGE);  // [2][2][QB] lse2, delta
+
+  int item_idx, kv;
+  if (!xcd_map(blockIdx.x, a.n_items, a.hkv, item_idx, kv)) return;
+  const KItem it = a.items[item_idx];
+  if (it.nk <= 0) return;
+  if (it.kind == 1 && a.dk_seed == nullptr) return;  // detached prompt: no seeds wanted
+  const T* ksrc = it.kind == 0 ? a.k : a.k_prompt;
+  const T* vsrc = it.kind == 0 ? a.v : a.v_prompt;
+
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int lr = l & 31, lh = l >> 5;
+  const int hp = a.hp;
+  const int tpb = QB / hp;  // query tokens per block
+  const size_t kv_stride = (size_t)a.hkv * D;
+
+  // K and V of this lane's key (operand row = key), kept for the whole loop.
+  Frag<T> kf[NKK], vf[NKK];
+  {
+    const int key = 32 * w + lr;
+    const bool ok = key < it.nk;
+    const size_t off = (size_t)(it.k0 + (ok ? key : 0)) * kv_stride + kv * D;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      if (ok) {
+        load_frag(kf[kk], ksrc + off + 16 * kk + 8 * lh);
+        load_frag(vf[kk], vsrc + off + 16 * kk + 8 * lh);
+      } else {
+        kf[kk].v = {};
+        vf[kk].v = {};
+      }
+    }
+  }
+
+  // Query block cursor: head sub-group hs, segment seg, block blk.
+  struct Cur {
+    int hs, seg, blk, nblk, q0, nq, qpad;
+  };
+  const int blk0 = it.causal ? (it.kpos / tpb) : 0;
+  auto seg_init = [&](Cur& c) {
+    c.q0 = a.seg_cu[c.seg];
+    c.nq = a.seg_cu[c.seg + 1] - c.q0;
+    c.qpad = a.seg_pad[c.seg];
+    c.nblk = (c.nq + tpb - 1) / tpb;
+    c.blk = blk0;
+  };
+  auto settle = [&](Cur& c) -> bool {  // move to the next non-empty block
+    while (true) {
+      if (c.hs >= a.nsub) return false;
+      if (c.seg < it.seg_hi && c.blk < c.nblk) return true;
+      if (c.seg < it.seg_hi) ++c.seg;
+      if (c.seg >= it.seg_hi) {
+        c.seg = it.seg_lo;
+        ++c.hs;
+        if (c.hs >= a.nsub || it.seg_lo >= it.seg_hi) return false;
+      }
+      seg_init(c);
+    }
+  };
+
+  u32x4 qst[QPER], gst[QPER], tqst[TPER], tgst[TPER];
+  float lst = 0.f;
+  auto gload = [&](const Cur& c) {
+    const int hg = kv * a.nsub + c.hs;
+    const int tok0 = c.blk * tpb;
+#pragma unroll
+    for (int i = 0; i < QPER; ++i) {
+      const int qi = tid + NT * i;
+      if (QCH % NT == 0 || qi < QCH) {
+        const int r = qi / NCHQ, ch = qi % NCHQ;
+        const int tok = tok0 + r / hp;
+        if (tok < c.nq) {
+          const size_t o = ((size_t)(c.q0 + tok) * a.hq + hg * hp + (r % hp)) * D + ch * CH;
+          qst[i] = *reinterpret_cast<const u32x4*>(a.q + o);
+          gst[i] = *reinterpret_cast<const u32x4*>(a.dout + o);
+        } else {
+          qst[i] = u32x4{0, 0, 0, 0};
+          gst[i] = u32x4{0, 0, 0, 0};
+        }
+      }
+    }
+    const size_t tb = (size_t)hg * D * a.qt_stride + (size_t)c.qpad * hp + (size_t)c.blk * QB;
+#pragma unroll
+    for (int i = 0; i < TPER; ++i) {
+      const int qi = tid + NT * i;
+      if (TCH % NT == 0 || qi < TCH) {
+        const int dd = qi / NCHT, ch = qi % NCHT;
+        const size_t o = tb + (size_t)dd * a.qt_stride + ch * CH;
+        tqst[i] = *reinterpret_cast<const u32x4*>(a.qt + o);
+        tgst[i] = *reinterpret_cast<const u32x4*>(a.dot + o);
+      }
+    }
+    if (tid < 2 * QB) {
+      const int r = tid & (QB - 1);
+      const int tok = tok0 + r / hp;
+      const size_t li = (size_t)(hg * hp + (r % hp)) * a.lse_stride + c.q0 + tok;
+      if (tid < QB) lst = tok < c.nq ? a.lse[li] * kLog2e : INFINITY;
+      else lst = tok < c.nq ? a.delta[li] : 0.f;
+    }
+  };
+  auto lstore = [&](int stage) {
+    T* qs = smem + stage * STAGE;
+    T* gs = qs + QTILE;
+    T* tqs = gs + QTILE;
+    T* tgs = tqs + QTILE;
+#pragma unroll
+    for (int i = 0; i < QPER; ++i) {
+      const int qi = tid + NT * i;
+      if (QCH % NT == 0 || qi < QCH) {
+        const int r = qi / NCHQ, ch = qi % NCHQ;
+        const int o = r * D + ((ch ^ swz_row<NCHQ>(r)) * CH);
+        *reinterpret_cast<u32x4*>(qs + o) = qst[i];
+        *reinterpret_cast<u32x4*>(gs + o) = gst[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < TPER; ++i) {
+      const int qi = tid + NT * i;
+      if (TCH % NT == 0 || qi < TCH) {
+        const int dd = qi / NCHT, ch = qi % NCHT;
+        const int o = dd * QB + ((ch ^ swz_row<NCHT>(dd)) * CH);
+        *reinterpret_cast<u32x4*>(tqs + o) = tqst[i];
+        *reinterpret_cast<u32x4*>(tgs + o) = tgst[i];
+      }
+    }
+    if (tid < 2 * QB) fsm[stage * 2 * QB + tid] = lst;
+  };
+
+  f32x16 dka[NDB], dva[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    dka[db] = f32x16{};
+    dva[db] = f32x16{};
+  }
+  const float c2 = a.scale_log2;
+  const int key_loc = it.kpos + 32 * w + lr;    // this lane's key, segment position
+  const int wave_kmax = it.kpos + 32 * w + 31;  // largest key position of the wave
+
+  Cur cur{0, it.seg_lo, 0, 0, 0, 0, 0};
+  bool have = false;
+  if (it.seg_lo < it.seg_hi) {
+    seg_init(cur);
+    have = settle(cur);
+  }
+  if (have) {
+    gload(cur);
+    lstore(0);
+  }
+  __syncthreads();
+  int stage = 0;
+  while (have) {
+    Cur nxt = cur;
+    ++nxt.blk;
+    const bool more = settle(nxt);
+    if (more) gload(nxt);
+    const T* qs = smem + stage * STAGE;
+    const T* gs = qs + QTILE;
+    const T* tqs = gs + QTILE;
+    const T* tgs = tqs + QTILE;
+    const float* lse_s = fsm + stage * 2 * QB;
+    const float* del_s = lse_s + QB;
+
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      Frag<T> qa, ga;
+      lds_frag(qa, qs, lr, D, 16 * kk + 8 * lh, swz_row<NCHQ>(lr));
+      lds_frag(ga, gs, lr, D, 16 * kk + 8 * lh, swz_row<NCHQ>(lr));
+      mma(s, qa, kf[kk]);
+      mma(dp, ga, vf[kk]);
+    }
+    // s: lane l, register jj -> query row 8*(jj/4) + 4*lh + jj%4, key lr.
+    const int tok0 = cur.blk * tpb;
+    const bool need_mask = it.causal && (tok0 < wave_kmax);
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int r0 = 8 * g4 + 4 * lh;
+      const f32x4 lv = *reinterpret_cast<const f32x4*>(lse_s + r0);
+      const f32x4 dv = *reinterpret_cast<const f32x4*>(del_s + r0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int jj = 4 * g4 + e;
+        float p = fast_exp2(s[jj] * c2 - lv[e]);
+        if (need_mask && key_loc > tok0 + (r0 + e) / hp) p = 0.f;
+        s[jj] = p;
+        dp[jj] = p * (dp[jj] - dv[e]);
+      }
+    }
+    Frag<T> pf[2], sf[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      to_frag(pf[hf], s, 8 * hf);
+      to_frag(sf[hf], dp, 8 * hf);
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int tr = 32 * db + lr;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        Frag<T> gt, qt;
+        lds_frag(gt, tgs, tr, QB, 16 * hf + 8 * lh, swz_row<NCHT>(tr));
+        lds_frag(qt, tqs, tr, QB, 16 * hf + 8 * lh, swz_row<NCHT>(tr));
+        mma(dva[db], pf[hf], gt);
+        mma(dka[db], sf[hf], qt);
+      }
+    }
+    if (more) lstore(stage ^ 1);
+    __syncthreads();
+    cur = nxt;
+    stage ^= 1;
+    have = more;
+  }
+
+  // dka/dva: lane l, register jj -> key 8*(jj/4) + 4*lh + jj%4 of this wave,
+  // column 32*db + lr.
+#pragma unroll
+  for (int jj = 0; jj < 16; ++jj) {
+    const int key = 32 * w + 8 * (jj >> 2) + 4 * lh + (jj & 3);
+    if (key >= it.nk) continue;
+    const size_t base = (size_t)(it.k0 + key) * kv_stride + kv * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const size_t o = base + 32 * db + lr;
+      float gk = dka[db][jj] * a.scale;
+      float gv = dva[db][jj];
+      if (it.kind == 1) {
+        a.dk_seed[o] = gk;
+        a.dv_seed[o] = gv;
+      } else {
+        if (it.kind == 2 && a.dk_seed != nullptr) {
+          gk += a.dk_seed[o];
+          gv += a.dv_seed[o];
+        }
+        a.dk[o] = from_f32<T>(gk);
+        a.dv[o] = from_f32<T>(gv);
+      }
+    }
+  }
+}
+
+template <typename T, int D>
+static hipError_t launch_dq_t(const DqLaunch& l, hipStream_t s) {
+  constexpr int KB = (sizeof(T) == 4 && D == 128) ? 1 : 2;
+  DqArgs<T, D> a;
+  a.q = static_cast<const T*>(l.q);
+  a.dout = static_cast<const T*>(l.dout);
+  a.lse = l.lse;
+  a.delta = l.delta;
+  a.dq = static_cast<T*>(l.dq);
+  a.k_a = static_cast<const T*>(l.k_a);
+  a.v_a = static_cast<const T*>(l.v_a);
+  a.kt_a = static_cast<const T*>(l.kt_a);
+  a.k_b = static_cast<const T*>(l.k_b);
+  a.v_b = static_cast<const T*>(l.v_b);
+  a.kt_b = static_cast<const T*>(l.kt_b);
+  a.items = static_cast<const QItem*>(l.items);
+  a.n_items = l.n_items;
+  a.hq = l.hq;
+  a.hkv = l.hkv;
+  a.hp = l.hp;
+  a.n_hg = l.hq / l.hp;
+  a.lse_stride = l.lse_stride;
+  a.kt_a_stride = l.kt_a_stride;
+  a.kt_b_stride = l.kt_b_stride;
+  a.scale_log2 = l.scale * kLog2e;
+  a.scale = l.scale;
+  const size_t smem = 2 * 3 * (size_t)(32 * KB) * D * sizeof(T);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(dq_kernel<T, D, KB>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  if (e != hipSuccess) return e;
+  const int grid = xcd_grid(l.n_items, a.n_hg);
+  if (grid <= 0) return hipSuccess;
+  hipEvent_t e0, e1;
+  kernel_events(kKernelDq, &e0, &e1);
+  if (e0) hipExtLaunchKernelGGL(dq_kernel<T, D, KB>, dim3(grid), dim3(512), smem, s, e0, e1, 0, a);
+  else dq_kernel<T, D, KB><<<dim3(grid), dim3(512), smem, s>>>(a);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_dkv_t(const DkvLaunch& l, hipStream_t s) {
+  DkvArgs<T, D> a;
+  a.k = static_cast<const T*>(l.k);
+  a.v = static_cast<const T*>(l.v);
+  a.k_prompt = static_cast<const T*>(l.k_prompt);
+  a.v_prompt = static_cast<const T*>(l.v_prompt);
+  a.q = static_cast<const T*>(l.q);
+  a.dout = static_cast<const T*>(l.dout);
+  a.qt = static_cast<const T*>(l.qt);
+  a.dot = static_cast<const T*>(l.dot);
+  a.lse = l.lse;
+  a.delta = l.delta;
+  a.seg_cu = l.seg_cu;
+  a.seg_pad = l.seg_pad;
+  a.dk = static_cast<T*>(l.dk);
+  a.dv = static_cast<T*>(l.dv);
+  a.dk_seed = l.dk_seed;
+  a.dv_seed = l.dv_seed;
+  a.items = static_cast<const KItem*>(l.items);
+  a.n_items = l.n_items;
+  a.hq = l.hq;
+  a.hkv = l.hkv;
+  a.hp = l.hp;
+  a.nsub = (l.hq / l.hkv) / l.hp;
+  a.lse_stride = l.lse_stride;
+  a.qt_stride = l.qt_stride;
+  a.scale_log2 = l.scale * kLog2e;
+  a.scale = l.scale;
+  const size_t smem = 2 * 4 * (size_t)32 * D * sizeof(T) + 2 * 2 * 32 * sizeof(float);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(dkv_kernel<T, D>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  if (e != hipSuccess) return e;
+  const int grid = xcd_grid(l.n_items, l.hkv);
+  if (grid <= 0) return hipSuccess;
+  hipEvent_t e0, e1;
+  kernel_events(kKernelDkv, &e0, &e1);
+  if (e0) hipExtLaunchKernelGGL(dkv_kernel<T, D>, dim3(grid), dim3(256), smem, s, e0, e1, 0, a);
+  else dkv_kernel<T, D><<<dim3(grid), dim3(256), smem, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dq(const DqLaunch& l, hipStream_t s) {
+  if (l.dtype == 1) return l.d == 128 ? launch_dq_t<bf16, 128>(l, s) : launch_dq_t<bf16, 64>(l, s);
+  return l.d == 128 ? launch_dq_t<float, 128>(l, s) : launch_dq_t<float, 64>(l, s);
+}
+
+hipError_t launch_dkv(const DkvLaunch& l, hipStream_t s) {
+  if (l.dtype == 1) return l.d == 128 ? launch_dkv_t<bf16, 128>(l, s) : launch_dkv_t<bf16, 64>(l, s);
+  return l.d == 128 ? launch_dkv_t<float, 128>(l, s) : launch_dkv_t<float, 64>(l, s);
+}
+
+}  // namespace treeattn

@@ -1,0 +1,293 @@
+// Query-stationary attention forward for gfx950: prompt prefill and response
+// replay (AugTree paper, section 3.2, "Shared prompt prefill pass" and
+// "Response replay"; tile semantics of section 2.2 / Fig. 3).
+//
+// One workgroup = 8 waves = 256 query rows of one head group.  A row is a
+// (token, head) pair: the hp query heads of a token that share one kv head
+// are packed next to each other, so every K/V tile staged in LDS feeds all of
+// them (GQA reuse).  Each wave owns 32 rows and keeps their Q in registers.
+// Keys stream through LDS in tiles of 64, double buffered: first segment A
+// (no mask: a replay row sees the whole prompt), then segment B (causal with
+// diagonal: prefill over the prompt, or the row's own branch in replay).  One
+// online-softmax state per row runs across both segments, so the prompt
+// column and the own-branch part are merged in registers (section 3.3: the
+// partial states along a query row are merged associatively).
+//
+// Scores are computed transposed, S^T = K Q^T, so each lane owns one query
+// row and 16 keys per 32-key block: the row maximum and sum are lane-local up
+// to one exchange with the other half of the wave.  The output is kept
+// transposed too, O^T += V^T P^T, with V^T read from a pre-transposed copy.
+#include <hip/hip_ext.h>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace treeattn {
+
+template <typename T, int D>
+struct FwdArgs {
+  const T* q;
+  T* o;
+  float* lse;
+  const T* k_a;
+  const T* vt_a;
+  const T* k_b;
+  const T* vt_b;
+  const QItem* items;
+  int n_items;
+  int hq, hkv, hp, n_hg;
+  int lse_stride;
+  int vt_a_stride, vt_b_stride;
+  float scale_log2;
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(512) void fwd_kernel(FwdArgs<T, D> a) {
+  constexpr int NT = 512, KT = kTileK, CH = ChunkOf<T>::kElems;
+  constexpr int NCHK = D / CH;        // 16-byte chunks per K row
+  constexpr int NCHV = KT / CH;       // chunks per V^T row
+  constexpr int KTILE = KT * D;       // elements per K (or V^T) tile
+  constexpr int KCH = KT * NCHK, VCH = D * NCHV;
+  constexpr int KPER = (KCH + NT - 1) / NT, VPER = (VCH + NT - 1) / NT;
+  constexpr int NKK = D / 16;         // contraction steps over d
+  constexpr int NDB = D / 32;         // 32-wide blocks of d
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  T* smem = reinterpret_cast<T*>(smem_raw);
+
+  int item_idx, hg;
+  if (!xcd_map(blockIdx.x, a.n_items, a.n_hg, item_idx, hg)) return;
+  const QItem it = a.items[item_idx];
+  if (it.nq <= 0) return;
+  const int grp = a.hq / a.hkv;
+  const int kv = (hg * a.hp) / grp;
+
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int lr = l & 31, lh = l >> 5;
+  const int row = 32 * w + lr;
+  const int tok = row / a.hp;
+  const int head = hg * a.hp + (row % a.hp);
+  const bool qvalid = tok < it.nq;
+
+  Frag<T> qf[NKK];
+  {
+    const T* qrow = a.q + ((size_t)(it.q0 + (qvalid ? tok : 0)) * a.hq + head) * D;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      if (qvalid) load_frag(qf[kk], qrow + 16 * kk + 8 * lh);
+      else qf[kk].v = {};
+    }
+  }
+
+  const int na = (it.alen + KT - 1) / KT;
+  const int nb = (it.blen + KT - 1) / KT;
+  const int total = na + nb;
+  const size_t kv_stride = (size_t)a.hkv * D;
+
+  u32x4 kst[KPER], vst[VPER];
+  auto gload = [&](int j) {
+    const bool inA = j < na;
+    const int ks = (inA ? j : j - na) * KT;
+    const T* kbase = inA ? a.k_a + (size_t)it.a0 * kv_stride : a.k_b + (size_t)it.b0 * kv_stride;
+    const int klen = inA ? it.alen : it.blen;
+#pragma unroll
+    for (int i = 0; i < KPER; ++i) {
+      const int qi = tid + NT * i;
+      if (KCH % NT == 0 || qi < KCH) {
+        const int r = qi / NCHK, c = qi % NCHK;
+        const int key = ks + r;
+        if (key < klen)
+          kst[i] = *reinterpret_cast<const u32x4*>(kbase + (size_t)key * kv_stride + kv * D + c * CH);
+        else
+          kst[i] = u32x4{0, 0, 0, 0};
+      }
+    }
+    const T* vbase = inA ? a.vt_a + (size_t)kv * D * a.vt_a_stride + it.apad + ks
+                         : a.vt_b + (size_t)kv * D * a.vt_b_stride + it.bpad + ks;
+    const int vstride = inA ? a.vt_a_stride : a.vt_b_stride;
+#pragma unroll
+    for (int i = 0; i < VPER; ++i) {
+      const int qi = tid + NT * i;
+      if (VCH % NT == 0 || qi < VCH) {
+        const int dd = qi / NCHV, c = qi % NCHV;
+        vst[i] = *reinterpret_cast<const u32x4*>(vbase + (size_t)dd * vstride + c * CH);
+      }
+    }
+  };
+  auto lstore = [&](int stage) {
+    T* kt = smem + stage * 2 * KTILE;
+    T* vt = kt + KTILE;
+#pragma unroll
+    for (int i = 0; i < KPER; ++i) {
+      const int qi = tid + NT * i;
+      if (KCH % NT == 0 || qi < KCH) {
+        const int r = qi / NCHK, c = qi % NCHK;
+        *reinterpret_cast<u32x4*>(kt + r * D + ((c ^ swz_row<NCHK>(r)) * CH)) = kst[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < VPER; ++i) {
+      const int qi = tid + NT * i;
+      if (VCH % NT == 0 || qi < VCH) {
+        const int dd = qi / NCHV, c = qi % NCHV;
+        *reinterpret_cast<u32x4*>(vt + dd * KT + ((c ^ swz_row<NCHV>(dd)) * CH)) = vst[i];
+      }
+    }
+  };
+
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+  float m_run = -INFINITY;  // running max of scaled scores, log2 units
+  float lsum = 0.f;         // this lane's share of the running normaliser
+  const float c2 = a.scale_log2;
+  const int wave_tok0 = (32 * w) / a.hp;  // smallest token index of this wave
+
+  if (total > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
+  for (int j = 0; j < total; ++j) {
+    if (j + 1 < total) gload(j + 1);
+    const T* kt = smem + (j & 1) * 2 * KTILE;
+    const T* vt = kt + KTILE;
+
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
+      const int kr = 32 * kb + lr;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        Frag<T> kf;
+        lds_frag(kf, kt, kr, D, 16 * kk + 8 * lh, swz_row<NCHK>(kr));
+        mma(s[kb], kf, qf[kk]);
+      }
+    }
+
+    const bool inA = j < na;
+    const int ks = (inA ? j : j - na) * KT;
+    const bool need_mask = inA ? (ks + KT > it.alen) : (ks + KT - 1 > it.qpos + wave_tok0);
+    if (need_mask) {
+      const int lim = inA ? it.alen - 1 : it.qpos + tok;  // last visible key
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) {
+          const int key = ks + 32 * kb + 8 * (jj >> 2) + 4 * lh + (jj & 3);
+          if (key > lim) s[kb][jj] = -INFINITY;
+        }
+    }
+
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) mx = fmaxf(mx, s[kb][jj]);
+    mx = max_with_other_half(mx) * c2;
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    m_run = m_new;
+    float ps = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) {
+        const float p = fast_exp2(s[kb][jj] * c2 - m_use);
+        s[kb][jj] = p;
+        ps += p;
+      }
+    lsum = lsum * alpha + ps;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+
+    Frag<T> pf[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) to_frag(pf[kb][hf], s[kb], 8 * hf);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int vr = 32 * db + lr;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          Frag<T> vf;
+          lds_frag(vf, vt, vr, KT, 16 * (2 * kb + hf) + 8 * lh, swz_row<NCHV>(vr));
+          mma(oacc[db], vf, pf[kb][hf]);
+        }
+    }
+
+    if (j + 1 < total) lstore((j + 1) & 1);
+    __syncthreads();
+  }
+
+  const float lt = sum_with_other_half(lsum);
+  if (!qvalid) return;
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  T* orow = a.o + ((size_t)(it.q0 + tok) * a.hq + head) * D;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d0 = 32 * db + 8 * g4 + 4 * lh;
+      if constexpr (sizeof(T) == 2) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = static_cast<bf16>(oacc[db][4 * g4 + e] * inv);
+        *reinterpret_cast<bf16x4*>(orow + d0) = v;
+      } else {
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = oacc[db][4 * g4 + e] * inv;
+        *reinterpret_cast<f32x4*>(orow + d0) = v;
+      }
+    }
+  if (lh == 0)
+    a.lse[(size_t)head * a.lse_stride + it.q0 + tok] =
+        lt > 0.f ? (m_run + fast_log2(lt)) * kLn2 : -INFINITY;
+}
+
+template <typename T, int D>
+static hipError_t launch_fwd_t(const FwdLaunch& l, hipStream_t s) {
+  FwdArgs<T, D> a;
+  a.q = static_cast<const T*>(l.q);
+  a.o = static_cast<T*>(l.o);
+  a.lse = l.lse;
+  a.k_a = static_cast<const T*>(l.k_a);
+  a.vt_a = static_cast<const T*>(l.vt_a);
+  a.k_b = static_cast<const T*>(l.k_b);
+  a.vt_b = static_cast<const T*>(l.vt_b);
+  a.items = static_cast<const QItem*>(l.items);
+  a.n_items = l.n_items;
+  a.hq = l.hq;
+  a.hkv = l.hkv;
+  a.hp = l.hp;
+  a.n_hg = l.hq / l.hp;
+  a.lse_stride = l.lse_stride;
+  a.vt_a_stride = l.vt_a_stride;
+  a.vt_b_stride = l.vt_b_stride;
+  a.scale_log2 = l.scale * kLog2e;
+  const size_t smem = 2 * 2 * (size_t)kTileK * D * sizeof(T);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fwd_kernel<T, D>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  if (e != hipSuccess) return e;
+  const int grid = xcd_grid(l.n_items, a.n_hg);
+  if (grid <= 0) return hipSuccess;
+  hipEvent_t e0, e1;
+  kernel_events(kKernelFwd, &e0, &e1);
+  if (e0) hipExtLaunchKernelGGL(fwd_kernel<T, D>, dim3(grid), dim3(512), smem, s, e0, e1, 0, a);
+  else fwd_kernel<T, D><<<dim3(grid), dim3(512), smem, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd(const FwdLaunch& l, hipStream_t s) {
+  if (l.dtype == 1) {
+    return l.d == 128 ? launch_fwd_t<bf16, 128>(l, s) : launch_fwd_t<bf16, 64>(l, s);
+  }
+  return l.d == 128 ? launch_fwd_t<float, 128>(l, s) : launch_fwd_t<float, 64>(l, s);
+}
+
+}  // namespace treeattn

@@ -1,0 +1,397 @@
+// Auxiliary kernels: the device-side work lists, transposed copies, the
+// backward row dot product, and the standalone partial-state merge.
+#include "device_common.h"
+#include "launch.h"
+
+namespace treeattn {
+
+// ------------------------------------------------------------ work lists
+//
+// One workgroup derives every tile of the launch from the device offset
+// arrays and writes them in decreasing cost (longest-processing-time first:
+// the heaviest tiles start first, which evens out the tail).  The same idea
+// orders replay units largest first in the AugTree planner (section 3.4).
+// Costs are counted in 64-key steps (query-stationary tiles) or 32-row
+// blocks (key-stationary tiles); a counting sort over at most kBuckets
+// levels keeps the order approximate for very long tiles.
+
+constexpr int kMetaThreads = 1024;
+constexpr int kBuckets = 2048;
+
+__device__ int block_exclusive_scan(int v, int* sh) {
+  // sh: kMetaThreads ints.  Returns the exclusive prefix; sh[last] holds the
+  // inclusive total afterwards (read it after a barrier).
+  const int t = threadIdx.x;
+  sh[t] = v;
+  __syncthreads();
+  for (int off = 1; off < kMetaThreads; off <<= 1) {
+    const int x = t >= off ? sh[t - off] : 0;
+    __syncthreads();
+    sh[t] += x;
+    __syncthreads();
+  }
+  return sh[t] - v;
+}
+
+// Writes out[i] = sum_{k<i} f(k) for i in [0, n] and returns the total.
+template <typename F>
+__device__ int scan_into(int n, F f, int32_t* out, int* sh) {
+  int carry = 0;
+  for (int base = 0; base < n; base += kMetaThreads) {
+    const int i = base + threadIdx.x;
+    const int v = i < n ? f(i) : 0;
+    const int ex = block_exclusive_scan(v, sh);
+    if (i < n) out[i] = carry + ex;
+    const int tot = sh[kMetaThreads - 1];
+    __syncthreads();
+    carry += tot;
+  }
+  if (threadIdx.x == 0) out[n] = carry;
+  __syncthreads();
+  return carry;
+}
+
+__device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+__device__ __forceinline__ int pad_len(int n) { return ceil_div(n, kPad) * kPad; }
+
+__global__ __launch_bounds__(kMetaThreads) void meta_kernel(MetaArgs a) {
+  __shared__ int sh[kMetaThreads];
+  __shared__ int hist[kBuckets];
+  __shared__ int cursor[kBuckets];
+  __shared__ int max_cost;
+  const int t = threadIdx.x;
+  const int ng = a.n_groups, nbr = a.n_branches;
+  const int32_t* pcu = a.prompt_cu;
+  const int32_t* gcu = a.group_branch_cu;
+  const int32_t* rcu = a.resp_cu;
+
+  // padded offsets of every segment in the transposed copies
+  scan_into(ng, [&](int g) { return pad_len(pcu[g + 1] - pcu[g]); }, a.prompt_pad, sh);
+  if (a.mode == kMetaQReplay || a.mode == kMetaKReplay) {
+    scan_into(nbr, [&](int i) { return pad_len(rcu[i + 1] - rcu[i]); }, a.resp_pad, sh);
+    for (int g = t; g < ng; g += kMetaThreads)
+      for (int i = gcu[g]; i < gcu[g + 1]; ++i) a.branch_group[i] = g;
+  }
+  __syncthreads();
+
+  // sources and their tile counts
+  const int tq = a.tile_q;
+  int nsrc = 0;
+  if (a.mode == kMetaQPrefill || a.mode == kMetaKPrefill) nsrc = ng;
+  else if (a.mode == kMetaQReplay) nsrc = nbr;
+  else nsrc = ng + nbr;
+  auto tiles_of = [&](int s) -> int {
+    switch (a.mode) {
+      case kMetaQPrefill: return ceil_div(pcu[s + 1] - pcu[s], tq);
+      case kMetaQReplay: return ceil_div(rcu[s + 1] - rcu[s], tq);
+      case kMetaKPrefill: return ceil_div(pcu[s + 1] - pcu[s], kTileKV);
+      default:
+        return s < ng ? ceil_div(pcu[s + 1] - pcu[s], kTileKV)
+                      : ceil_div(rcu[s - ng + 1] - rcu[s - ng], kTileKV);
+    }
+  };
+  int n = scan_into(nsrc, tiles_of, a.src_cu, sh);
+  if (n > a.cap) n = a.cap;
+  const bool qmode = a.mode == kMetaQPrefill || a.mode == kMetaQReplay;
+  QItem* qtmp = static_cast<QItem*>(a.items_tmp);
+  KItem* ktmp = static_cast<KItem*>(a.items_tmp);
+  QItem* qout = static_cast<QItem*>(a.items);
+  KItem* kout = static_cast<KItem*>(a.items);
+
+  if (t == 0) max_cost = 0;
+  for (int b = t; b < kBuckets; b += kMetaThreads) {
+    hist[b] = 0;
+    cursor[b] = 0;
+  }
+  // empty items everywhere first, so a short list never leaves stale slots
+  for (int i = t; i < a.cap; i += kMetaThreads) {
+    if (qmode) qout[i] = QItem{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    else kout[i] = KItem{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+  __syncthreads();
+
+  for (int i = t; i < n; i += kMetaThreads) {
+    int lo = 0, hi = nsrc - 1;  // last source with src_cu[s] <= i
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.src_cu[mid] <= i) lo = mid;
+      else hi = mid - 1;
+    }
+    const int s = lo, tile = i - a.src_cu[s];
+    int cost;
+    if (qmode) {
+      QItem q;
+      q.r0 = q.r1 = 0;
+      if (a.mode == kMetaQPrefill) {
+        const int plen = pcu[s + 1] - pcu[s];
+        q.qpos = tile * tq;
+        q.nq = min(tq, plen - q.qpos);
+        q.q0 = pcu[s] + q.qpos;
+        q.a0 = 0;
+        q.alen = 0;
+        q.apad = 0;
+        q.b0 = pcu[s];
+        q.blen = q.qpos + q.nq;
+        q.bpad = a.prompt_pad[s];
+      } else {
+        const int g = a.branch_group[s];
+        const int rlen = rcu[s + 1] - rcu[s];
+        q.qpos = tile * tq;
+        q.nq = min(tq, rlen - q.qpos);
+        q.q0 = rcu[s] + q.qpos;
+        q.a0 = pcu[g];
+        q.alen = pcu[g + 1] - pcu[g];
+        q.apad = a.prompt_pad[g];
+        q.b0 = rcu[s];
+        q.blen = q.qpos + q.nq;
+        q.bpad = a.resp_pad[s];
+      }
+      cost = ceil_div(q.alen, kTileK) + ceil_div(q.blen, kTileK);
+      q.cost = cost;
+      qtmp[i] = q;
+    } else {
+      KItem k;
+      if (a.mode == kMetaKPrefill) {
+        const int plen = pcu[s + 1] - pcu[s];
+        k.kpos = tile * kTileKV;
+        k.nk = min(kTileKV, plen - k.kpos);
+        k.k0 = pcu[s] + k.kpos;
+        k.kind = 2;
+        k.seg_lo = s;
+        k.seg_hi = s + 1;
+        k.causal = 1;
+        cost = plen - k.kpos;
+      } else if (s < ng) {  // prompt tile in replay: every branch of the group
+        const int plen = pcu[s + 1] - pcu[s];
+        k.kpos = tile * kTileKV;
+        k.nk = min(kTileKV, plen - k.kpos);
+        k.k0 = pcu[s] + k.kpos;
+        k.kind = 1;
+        k.seg_lo = gcu[s];
+        k.seg_hi = gcu[s + 1];
+        k.causal = 0;
+        cost = rcu[gcu[s + 1]] - rcu[gcu[s]];
+      } else {  // own-branch tile
+        const int b = s - ng;
+        const int rlen = rcu[b + 1] - rcu[b];
+        k.kpos = tile * kTileKV;
+        k.nk = min(kTileKV, rlen - k.kpos);
+        k.k0 = rcu[b] + k.kpos;
+        k.kind = 0;
+        k.seg_lo = b;
+        k.seg_hi = b + 1;
+        k.causal = 1;
+        cost = rlen - k.kpos;
+      }
+      cost = ceil_div(cost, 32);
+      k.cost = cost;
+      ktmp[i] = k;
+    }
+    atomicMax(&max_cost, cost);
+  }
+  __syncthreads();
+  const int mc = max_cost;
+  auto bucket_of = [&](int c) -> int {
+    // larger cost -> smaller bucket index (sorted first)
+    const long long b = (long long)(mc - c) * (kBuckets - 1) / (mc > 0 ? mc : 1);
+    return (int)(b < 0 ? 0 : (b > kBuckets - 1 ? kBuckets - 1 : b));
+  };
+  for (int i = t; i < n; i += kMetaThreads)
+    atomicAdd(&hist[bucket_of(qmode ? qtmp[i].cost : ktmp[i].cost)], 1);
+  __syncthreads();
+  // exclusive scan of hist (kBuckets = 2 * kMetaThreads entries)
+  {
+    const int b0 = 2 * t, b1 = 2 * t + 1;
+    const int v = hist[b0] + hist[b1];
+    const int ex = block_exclusive_scan(v, sh);
+    __syncthreads();
+    const int h0 = hist[b0];
+    __syncthreads();
+    hist[b0] = ex;
+    hist[b1] = ex + h0;
+  }
+  __syncthreads();
+  for (int i = t; i < n; i += kMetaThreads) {
+    const int c = qmode ? qtmp[i].cost : ktmp[i].cost;
+    const int b = bucket_of(c);
+    const int pos = hist[b] + atomicAdd(&cursor[b], 1);
+    if (pos < a.cap) {
+      if (qmode) qout[pos] = qtmp[i];
+      else kout[pos] = ktmp[i];
+    }
+  }
+}
+
+hipError_t launch_meta(const MetaArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(meta_kernel, dim3(1), dim3(kMetaThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ transpose
+//
+// out[hg][d][perm(col)] for 64 columns per workgroup.  Column col of head
+// group hg is token u = (col - pad[s]*hp) / hp of segment s and head
+// hg*hp + col % hp; padding columns are written as zeros.
+
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_kernel(TransposeArgs a) {
+  constexpr int C = 64;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  T* tile = reinterpret_cast<T*>(smem_raw);  // [C][d + 8]
+  const int ld = a.d + 8;
+  const int cb = blockIdx.x, hg = blockIdx.y;
+  const int col0 = cb * C;
+  const int hp = a.hp;
+  // segment containing col0 (segments are kPad-token aligned in columns)
+  int lo = 0, hi = a.n_seg - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.seg_pad[mid] * hp <= col0) lo = mid;
+    else hi = mid - 1;
+  }
+  const int s = lo;
+  const int seg_len = a.seg_cu[s + 1] - a.seg_cu[s];
+  const int u0 = (col0 - a.seg_pad[s] * hp) / hp;
+  const T* in = static_cast<const T*>(a.in);
+  T* out = static_cast<T*>(a.out);
+  constexpr int CH = 16 / sizeof(T);
+  const int nch = a.d / CH;
+  for (int q = threadIdx.x; q < C * nch; q += 256) {
+    const int c = q / nch, ch = q % nch;
+    const int u = u0 + c / hp;
+    u32x4 v = u32x4{0, 0, 0, 0};
+    if (u < seg_len)
+      v = *reinterpret_cast<const u32x4*>(
+          in + ((size_t)(a.seg_cu[s] + u) * a.heads + hg * hp + c % hp) * a.d + ch * CH);
+    *reinterpret_cast<u32x4*>(tile + c * ld + ch * CH) = v;
+  }
+  __syncthreads();
+  const size_t stride = (size_t)a.pad_tokens * hp;
+  for (int q = threadIdx.x; q < a.d * (C / CH); q += 256) {
+    const int dd = q / (C / CH), ch = q % (C / CH);
+    T vals[CH];
+#pragma unroll
+    for (int e = 0; e < CH; ++e) {
+      const int pos = ch * CH + e;              // stored position in the 64 columns
+      const int src = (pos & ~15) | perm16(pos & 15);  // column held there
+      vals[e] = tile[src * ld + dd];
+    }
+    *reinterpret_cast<u32x4*>(out + ((size_t)hg * a.d + dd) * stride + col0 + ch * CH) =
+        *reinterpret_cast<const u32x4*>(vals);
+  }
+}
+
+hipError_t launch_transpose(const TransposeArgs& a, int dtype, hipStream_t s) {
+  const int cols = a.pad_tokens * a.hp;
+  if (cols == 0) return hipSuccess;
+  dim3 grid(cols / 64, a.heads / a.hp);
+  const size_t esz = dtype == 1 ? 2 : 4;
+  const size_t smem = 64 * (size_t)(a.d + 8) * esz;
+  if (dtype == 1) hipLaunchKernelGGL(transpose_kernel<bf16>, grid, dim3(256), smem, s, a);
+  else hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(256), smem, s, a);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ row dot
+// delta[h][t] = sum_c dout[t][h][c] * out[t][h][c]; 16 lanes per row.
+
+template <typename T>
+__global__ __launch_bounds__(256) void row_dot_kernel(const T* dout, const T* out, float* delta,
+                                                      int tokens, int heads, int d) {
+  constexpr int CH = 16 / sizeof(T);
+  const int lanes = d / CH;  // 16 (bf16, d=128) ... 4 (fp32, d=64)... per row
+  const int gid = blockIdx.x * 256 + threadIdx.x;
+  const int row = gid / 16, part = gid % 16;
+  const bool ok = row < tokens * heads;
+  float acc = 0.f;
+  if (ok) {
+    const size_t base = (size_t)row * d;
+    for (int ch = part; ch < lanes; ch += 16) {
+      T a[CH], b[CH];
+      *reinterpret_cast<u32x4*>(a) = *reinterpret_cast<const u32x4*>(dout + base + ch * CH);
+      *reinterpret_cast<u32x4*>(b) = *reinterpret_cast<const u32x4*>(out + base + ch * CH);
+#pragma unroll
+      for (int e = 0; e < CH; ++e) acc += to_f32(a[e]) * to_f32(b[e]);
+    }
+  }
+#pragma unroll
+  for (int off = 8; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 16);
+  if (ok && part == 0) {
+    const int t = row / heads, h = row % heads;
+    delta[(size_t)h * tokens + t] = acc;
+  }
+}
+
+hipError_t launch_row_dot(const void* dout, const void* out, float* delta, int tokens, int heads,
+                          int d, int dtype, hipStream_t s) {
+  const long long rows = (long long)tokens * heads;
+  if (rows == 0) return hipSuccess;
+  const int grid = (int)((rows * 16 + 255) / 256);
+  if (dtype == 1)
+    hipLaunchKernelGGL(row_dot_kernel<bf16>, dim3(grid), dim3(256), 0, s,
+                       static_cast<const bf16*>(dout), static_cast<const bf16*>(out), delta,
+                       tokens, heads, d);
+  else
+    hipLaunchKernelGGL(row_dot_kernel<float>, dim3(grid), dim3(256), 0, s,
+                       static_cast<const float*>(dout), static_cast<const float*>(out), delta,
+                       tokens, heads, d);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ lse_merge
+// Partial states (O_k normalised, LSE_k): LSE = ln sum_k exp(LSE_k),
+// O = sum_k exp(LSE_k - LSE) O_k (AugTree paper, section 3.3 and Fig. 8).
+// 16 lanes per (row, head), 8 (d = 128) or 4 (d = 64) elements per lane.
+
+template <typename T>
+__global__ __launch_bounds__(256) void lse_merge_kernel(int splits, int rows, int heads, int d,
+                                                        const float* o_parts,
+                                                        const float* lse_parts, T* o_out,
+                                                        float* lse_out) {
+  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long item = gid / 16;
+  const int part = (int)(gid % 16);
+  if (item >= (long long)rows * heads) return;
+  const int r = (int)(item / heads), h = (int)(item % heads);
+  const size_t lstride = (size_t)heads * rows;
+  const size_t li = (size_t)h * rows + r;
+  float mx = -INFINITY;
+  for (int k = 0; k < splits; ++k) mx = fmaxf(mx, lse_parts[k * lstride + li]);
+  const int per = d / 16;  // elements per lane
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  float wsum = 0.f;
+  if (mx != -INFINITY) {
+    const size_t ostride = (size_t)rows * heads * d;
+    const size_t ob = ((size_t)r * heads + h) * d + part * per;
+    for (int k = 0; k < splits; ++k) {
+      const float lk = lse_parts[k * lstride + li];
+      const float wk = lk == -INFINITY ? 0.f : fast_exp2((lk - mx) * kLog2e);
+      wsum += wk;
+      if (wk != 0.f) {
+        const float* src = o_parts + k * ostride + ob;
+        for (int e = 0; e < per; ++e) acc[e] += wk * src[e];
+      }
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  T* dst = o_out + ((size_t)r * heads + h) * d + part * per;
+  for (int e = 0; e < per; ++e) dst[e] = from_f32<T>(acc[e] * inv);
+  if (part == 0) lse_out[li] = mx == -INFINITY ? -INFINITY : mx + fast_log2(wsum) * kLn2;
+}
+
+hipError_t launch_lse_merge(int splits, int rows, int heads, int d, int out_dtype,
+                            const float* o_parts, const float* lse_parts, void* o_out,
+                            float* lse_out, hipStream_t s) {
+  const long long n = (long long)rows * heads * 16;
+  if (n == 0) return hipSuccess;
+  const int grid = (int)((n + 255) / 256);
+  if (out_dtype == 1)
+    hipLaunchKernelGGL(lse_merge_kernel<bf16>, dim3(grid), dim3(256), 0, s, splits, rows, heads,
+                       d, o_parts, lse_parts, static_cast<bf16*>(o_out), lse_out);
+  else
+    hipLaunchKernelGGL(lse_merge_kernel<float>, dim3(grid), dim3(256), 0, s, splits, rows, heads,
+                       d, o_parts, lse_parts, static_cast<float*>(o_out), lse_out);
+  return hipGetLastError();
+}
+
+}  // namespace treeattn

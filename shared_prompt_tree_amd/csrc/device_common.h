@@ -1,0 +1,188 @@
+// Device helpers shared by the gfx950 attention kernels.
+//
+// Matrix products use the 32x32 MFMA output block.  For the bf16 path one
+// v_mfma_f32_32x32x16_bf16 covers a 16-deep slice of the contraction; for the
+// float32 path eight v_mfma_f32_32x32x2_f32 cover the same slice.  Operand
+// fragments are 8 elements per lane along the contraction axis: lane l holds
+// row (l % 32) of its operand and contraction slots 8*(l/32) .. 8*(l/32)+7.
+// Which hardware k index a slot lands on does not matter as long as both
+// operands use the same (l/32, element) -> contraction-index assignment,
+// which every product here does.
+//
+// Output block layout (32x32, 16 float32 per lane): lane l, register j holds
+// row 8*(j/4) + 4*(l/32) + (j%4) and column l % 32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace treeattn {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Eight contraction elements of one operand row, per lane.
+template <typename T>
+struct Frag;
+template <>
+struct Frag<bf16> {
+  bf16x8 v;
+};
+template <>
+struct Frag<float> {
+  f32x8 v;
+};
+
+__device__ __forceinline__ void mma(f32x16& c, const Frag<bf16>& a, const Frag<bf16>& b) {
+  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v, b.v, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ void mma(f32x16& c, const Frag<float>& a, const Frag<float>& b) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.v[s], b.v[s], c, 0, 0, 0);
+}
+
+// Bytes per 16-byte chunk and elements per chunk.
+template <typename T>
+struct ChunkOf {
+  static constexpr int kElems = 16 / sizeof(T);
+};
+
+// Load 8 contiguous elements (16-byte aligned for bf16, 32-byte for float).
+__device__ __forceinline__ void load_frag(Frag<bf16>& f, const bf16* p) {
+  f.v = *reinterpret_cast<const bf16x8*>(p);
+}
+__device__ __forceinline__ void load_frag(Frag<float>& f, const float* p) {
+  f.v = *reinterpret_cast<const f32x8*>(p);
+}
+
+// Fragment read from an LDS tile stored in 16-byte chunks with an XOR
+// swizzle: element e of row r lives at chunk slot ((e / CH) ^ swz) of that
+// row, where CH is the chunk size in elements.
+template <typename T>
+__device__ __forceinline__ void lds_frag(Frag<T>& f, const T* tile, int row, int row_elems,
+                                         int elem0, int swz) {
+  constexpr int CH = ChunkOf<T>::kElems;
+  const T* base = tile + row * row_elems;
+  if constexpr (CH == 8) {
+    f.v = *reinterpret_cast<const bf16x8*>(base + (((elem0 / CH) ^ swz) * CH));
+  } else {
+    f32x4 lo = *reinterpret_cast<const f32x4*>(base + (((elem0 / CH) ^ swz) * CH));
+    f32x4 hi = *reinterpret_cast<const f32x4*>(base + ((((elem0 / CH) + 1) ^ swz) * CH));
+    f.v = f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+}
+
+// Chunk-slot XOR for an LDS tile row of NCH 16-byte chunks.  Rows of 256
+// bytes or more are spread by r mod NCH; shorter rows share a 256-byte bank
+// window with their neighbours and are spread by r / (16 / NCH), so any 16
+// consecutive rows read at one chunk index hit 16 different bank groups.
+template <int NCH>
+__device__ __forceinline__ int swz_row(int r) {
+  if constexpr (NCH >= 16) return r & (NCH - 1);
+  else return (r / (16 / NCH)) & (NCH - 1);
+}
+
+// Convert 8 float32 (registers j0..j0+7 of an output block) to an operand
+// fragment.  bf16 rounds to nearest even.
+__device__ __forceinline__ void to_frag(Frag<bf16>& f, const f32x16& c, int j0) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f.v[e] = static_cast<bf16>(c[j0 + e]);
+}
+__device__ __forceinline__ void to_frag(Frag<float>& f, const f32x16& c, int j0) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f.v[e] = c[j0 + e];
+}
+
+__device__ __forceinline__ float to_f32(bf16 x) { return static_cast<float>(x); }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+template <typename T>
+__device__ __forceinline__ T from_f32(float x) {
+  return static_cast<T>(x);
+}
+
+// Values of lane l and lane l ^ 32 (the other half of the wave).
+// v_permlane32_swap exchanges the upper half of its first operand with the
+// lower half of its second; called with the same value twice it returns the
+// pair (own, other) in some order on every lane.
+__device__ __forceinline__ float max_with_other_half(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_with_other_half(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Position of row/key index k inside its 16-aligned group in the transposed
+// copies: bits 2 and 3 are exchanged.  The output block holds rows
+// {4*(l/32) + (j%4)} + 8*(j/4); with the exchange, the 8 slots one lane
+// feeds to a 16-deep product (registers 8h .. 8h+7) become 8 consecutive
+// positions 8*(l/32) .. 8*(l/32)+7 of the 16-group.
+__host__ __device__ __forceinline__ int perm16(int k) {
+  return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
+}
+
+// Workgroup -> (work item, head group) with all head groups of a kv head on
+// one XCD.  Workgroups are dealt to the 8 XCDs round-robin (block b runs on
+// XCD b % 8), and each XCD has its own L2.
+__device__ __forceinline__ bool xcd_map(int b, int n_items, int n_hg, int& item, int& hg) {
+  const int x = b & 7, j = b >> 3;
+  if (n_hg % 8 == 0) {
+    const int per = n_hg / 8;
+    hg = x * per + (j % per);
+    item = j / per;
+  } else if (8 % n_hg == 0) {
+    const int per = 8 / n_hg;
+    hg = x % n_hg;
+    item = j * per + x / n_hg;
+  } else {
+    hg = b % n_hg;
+    item = b / n_hg;
+  }
+  return item < n_items;
+}
+
+__host__ __device__ inline int xcd_grid(int n_items, int n_hg) {
+  if (n_hg % 8 == 0 || 8 % n_hg != 0) return n_items * n_hg;
+  const int per = 8 / n_hg;
+  return ((n_items + per - 1) / per) * 8;
+}
+
+// Work items built on the device from the offset arrays.
+// Query-stationary item: a tile of query tokens and the two key segments it
+// reads: segment A without mask (the prompt, for replay) and segment B with
+// the causal mask (the prompt for prefill, the own branch for replay).
+struct QItem {
+  int q0, nq, qpos;      // first query token (global), tokens in tile, position in B
+  int a0, alen, apad;    // segment A: first key token, keys, padded offset
+  int b0, blen, bpad;    // segment B: first key token, keys read, padded offset
+  int cost, r0, r1;
+};
+
+// Key-stationary item: a tile of key tokens and the query segments
+// [seg_lo, seg_hi) that read it.
+struct KItem {
+  int k0, nk, kpos;      // first key token (global), keys, position in its segment
+  int kind;              // 0: write I/O dtype; 1: write float32 seeds; 2: I/O dtype + seeds
+  int seg_lo, seg_hi, causal, cost;
+};
+
+constexpr int kTileQ = 256;  // query rows per workgroup (query-stationary)
+constexpr int kTileK = 64;   // keys per step (query-stationary)
+constexpr int kTileKV = 128; // keys per workgroup (key-stationary)
+constexpr int kBlockQ = 64;  // query rows per step (key-stationary)
+constexpr int kPad = 64;     // token padding of every segment in transposed copies
+
+}  // namespace treeattn

@@ -1,0 +1,572 @@
+// C ABI of libtreeattn.so (declared in include/tree_attn.h).
+//
+// Every entry point validates its arguments on the host before the first
+// HIP call, lays out the caller's workspace, and enqueues:
+//   prefill      : work list, V^T copy, forward kernel
+//   replay_fwd   : work list, V^T copies, forward kernel (prompt column and
+//                  own branch merged in one online-softmax state)
+//   replay_bwd   : delta, work lists, K^T / Q^T / dO^T copies, dQ kernel,
+//                  dK/dV kernel (prompt tiles write float32 seeds summed over
+//                  every branch; own-branch tiles write dK_R, dV_R)
+//   prefill_bwd  : delta, work lists, K^T / Q^T / dO^T copies, dQ kernel,
+//                  dK/dV kernel (prefill term plus the seeds)
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "../../include/tree_attn.h"
+#include "device_common.h"
+#include "launch.h"
+
+using namespace treeattn;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+int pad_len(int n) { return ceil_div(n, kPad) * kPad; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// Host-side facts derived from the problem after validation.
+struct Shape {
+  int ng = 0, nb = 0, hq = 0, hkv = 0, d = 0, dtype = 0, hp = 1, tile_q = 0;
+  size_t esz = 0;
+  long long p_tokens = 0, r_tokens = 0;
+  long long p_pad = 0, r_pad = 0;    // padded token totals
+  long long q_items_prefill = 0, q_items_replay = 0;
+  long long k_items_prefill = 0, k_items_replay = 0;
+};
+
+int validate_problem(const tree_attn_problem* p, bool need_device, Shape& s) {
+  if (!p) return TREE_ATTN_ERR_INVALID;
+  if (p->dtype != TREE_ATTN_F32 && p->dtype != TREE_ATTN_BF16) return TREE_ATTN_ERR_UNSUPPORTED;
+  if (p->head_dim != 64 && p->head_dim != 128) return TREE_ATTN_ERR_UNSUPPORTED;
+  if (p->num_groups < 1 || p->num_branches < 0) return TREE_ATTN_ERR_INVALID;
+  if (p->num_q_heads < 1 || p->num_kv_heads < 1) return TREE_ATTN_ERR_INVALID;
+  if (p->num_q_heads % p->num_kv_heads != 0) return TREE_ATTN_ERR_INVALID;
+  if (!(p->softmax_scale > 0.f) || !std::isfinite(p->softmax_scale)) return TREE_ATTN_ERR_INVALID;
+  if (!p->prompt_cu_h || !p->group_branch_cu_h || !p->resp_cu_h) return TREE_ATTN_ERR_INVALID;
+  if (need_device && (!p->prompt_cu_d || !p->group_branch_cu_d || !p->resp_cu_d))
+    return TREE_ATTN_ERR_INVALID;
+  const int ng = p->num_groups, nb = p->num_branches;
+  if (p->prompt_cu_h[0] != 0 || p->group_branch_cu_h[0] != 0 || p->resp_cu_h[0] != 0)
+    return TREE_ATTN_ERR_INVALID;
+  for (int g = 0; g < ng; ++g) {
+    if (p->prompt_cu_h[g + 1] < p->prompt_cu_h[g]) return TREE_ATTN_ERR_INVALID;
+    if (p->group_branch_cu_h[g + 1] < p->group_branch_cu_h[g]) return TREE_ATTN_ERR_INVALID;
+  }
+  if (p->group_branch_cu_h[ng] != nb) return TREE_ATTN_ERR_INVALID;
+  for (int i = 0; i < nb; ++i)
+    if (p->resp_cu_h[i + 1] < p->resp_cu_h[i]) return TREE_ATTN_ERR_INVALID;
+
+  s.ng = ng;
+  s.nb = nb;
+  s.hq = p->num_q_heads;
+  s.hkv = p->num_kv_heads;
+  s.d = p->head_dim;
+  s.dtype = p->dtype;
+  s.esz = p->dtype == TREE_ATTN_BF16 ? 2 : 4;
+  const int grp = s.hq / s.hkv;
+  s.hp = 1;
+  while (s.hp < 16 && grp % (2 * s.hp) == 0) s.hp *= 2;
+  s.tile_q = kTileQ / s.hp;
+  s.p_tokens = p->prompt_cu_h[ng];
+  s.r_tokens = p->resp_cu_h[nb];
+  for (int g = 0; g < ng; ++g) {
+    const int len = p->prompt_cu_h[g + 1] - p->prompt_cu_h[g];
+    s.p_pad += pad_len(len);
+    s.q_items_prefill += ceil_div(len, s.tile_q);
+    s.k_items_prefill += ceil_div(len, kTileKV);
+  }
+  s.k_items_replay = s.k_items_prefill;
+  for (int i = 0; i < nb; ++i) {
+    const int len = p->resp_cu_h[i + 1] - p->resp_cu_h[i];
+    s.r_pad += pad_len(len);
+    s.q_items_replay += ceil_div(len, s.tile_q);
+    s.k_items_replay += ceil_div(len, kTileKV);
+  }
+  // every index the kernels form must fit in int32
+  const long long lim = (1LL << 31) - 1;
+  if (s.p_pad * s.hp > lim || s.r_pad * s.hp > lim) return TREE_ATTN_ERR_INVALID;
+  if ((s.p_tokens + s.r_tokens) * (long long)s.hq > lim) return TREE_ATTN_ERR_INVALID;
+  return TREE_ATTN_OK;
+}
+
+// Bump allocator over the caller's workspace.
+struct Carve {
+  char* base;
+  size_t off = 0;
+  explicit Carve(void* b) : base(static_cast<char*>(b)) {}
+  void* take(size_t bytes) {
+    void* p = base ? base + off : nullptr;
+    off += align_up(bytes);
+    return p;
+  }
+};
+
+struct MetaBufs {
+  int32_t* prompt_pad;
+  int32_t* resp_pad;
+  int32_t* branch_group;
+  int32_t* src_cu;
+  void* tmp;
+  void* items;
+};
+
+MetaBufs take_meta(Carve& c, const Shape& s, long long cap, size_t item_bytes) {
+  MetaBufs m;
+  m.prompt_pad = static_cast<int32_t*>(c.take((s.ng + 1) * sizeof(int32_t)));
+  m.resp_pad = static_cast<int32_t*>(c.take((s.nb + 1) * sizeof(int32_t)));
+  m.branch_group = static_cast<int32_t*>(c.take((s.nb + 1) * sizeof(int32_t)));
+  m.src_cu = static_cast<int32_t*>(c.take((s.ng + s.nb + 1) * sizeof(int32_t)));
+  m.tmp = c.take(std::max<long long>(cap, 1) * item_bytes);
+  m.items = c.take(std::max<long long>(cap, 1) * item_bytes);
+  return m;
+}
+
+// Workspace layout of one entry point.  With base == nullptr only the size
+// is computed.
+struct Plan {
+  MetaBufs mq{}, mk{};
+  void* vt_p = nullptr;   // V^T prompt  [hkv][d][p_pad]
+  void* vt_r = nullptr;   // V^T response
+  void* kt_p = nullptr;   // K^T prompt
+  void* kt_r = nullptr;   // K^T response
+  void* qt = nullptr;     // Q^T  [hq/hp][d][pad*hp]
+  void* dot = nullptr;    // dO^T
+  float* delta = nullptr; // [hq][tokens]
+  size_t bytes = 0;
+};
+
+Plan make_plan(const Shape& s, int op, void* base) {
+  Plan pl;
+  Carve c(base);
+  const size_t e = s.esz;
+  const size_t kvT_p = (size_t)s.hkv * s.d * s.p_pad * e;
+  const size_t kvT_r = (size_t)s.hkv * s.d * s.r_pad * e;
+  switch (op) {
+    case TREE_ATTN_OP_PREFILL:
+      pl.mq = take_meta(c, s, s.q_items_prefill, sizeof(QItem));
+      pl.vt_p = c.take(kvT_p);
+      break;
+    case TREE_ATTN_OP_REPLAY_FWD:
+      pl.mq = take_meta(c, s, s.q_items_replay, sizeof(QItem));
+      pl.vt_p = c.take(kvT_p);
+      pl.vt_r = c.take(kvT_r);
+      break;
+    case TREE_ATTN_OP_REPLAY_BWD:
+      pl.mq = take_meta(c, s, s.q_items_replay, sizeof(QItem));
+      pl.mk = take_meta(c, s, s.k_items_replay, sizeof(KItem));
+      pl.kt_p = c.take(kvT_p);
+      pl.kt_r = c.take(kvT_r);
+      pl.qt = c.take((size_t)s.hq * s.d * s.r_pad * e);
+      pl.dot = c.take((size_t)s.hq * s.d * s.r_pad * e);
+      pl.delta = static_cast<float*>(c.take((size_t)s.hq * s.r_tokens * sizeof(float)));
+      break;
+    case TREE_ATTN_OP_PREFILL_BWD:
+      pl.mq = take_meta(c, s, s.q_items_prefill, sizeof(QItem));
+      pl.mk = take_meta(c, s, s.k_items_prefill, sizeof(KItem));
+      pl.kt_p = c.take(kvT_p);
+      pl.qt = c.take((size_t)s.hq * s.d * s.p_pad * e);
+      pl.dot = c.take((size_t)s.hq * s.d * s.p_pad * e);
+      pl.delta = static_cast<float*>(c.take((size_t)s.hq * s.p_tokens * sizeof(float)));
+      break;
+    default:
+      break;
+  }
+  pl.bytes = c.off;
+  return pl;
+}
+
+int check_ws(const Shape& s, int op, void* ws, size_t ws_bytes, Plan& pl) {
+  pl = make_plan(s, op, nullptr);
+  if (ws_bytes < pl.bytes) return TREE_ATTN_ERR_WORKSPACE;
+  if (pl.bytes > 0 && !ws) return TREE_ATTN_ERR_INVALID;
+  if (!aligned16(ws)) return TREE_ATTN_ERR_INVALID;
+  pl = make_plan(s, op, ws);
+  return TREE_ATTN_OK;
+}
+
+// A tensor pointer must be non-null and 16-byte aligned unless it has no
+// element at all.
+bool tensor_ok(const void* p, long long tokens) {
+  if (tokens == 0) return true;
+  return p != nullptr && aligned16(p);
+}
+
+thread_local hipError_t g_last_hip = hipSuccess;
+thread_local hipEvent_t g_events[3][2] = {{nullptr, nullptr}, {nullptr, nullptr}, {nullptr, nullptr}};
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return TREE_ATTN_OK;
+  g_last_hip = e;
+  return TREE_ATTN_ERR_HIP;
+}
+
+#define TA_TRY(expr)                          \
+  do {                                        \
+    hipError_t e_ = (expr);                   \
+    if (e_ != hipSuccess) return hip_status(e_); \
+  } while (0)
+
+hipError_t run_meta(const tree_attn_problem* p, const Shape& s, const MetaBufs& m, int mode,
+                    long long cap, hipStream_t st) {
+  MetaArgs a;
+  a.mode = mode;
+  a.n_groups = s.ng;
+  a.n_branches = s.nb;
+  a.prompt_cu = p->prompt_cu_d;
+  a.group_branch_cu = p->group_branch_cu_d;
+  a.resp_cu = p->resp_cu_d;
+  a.prompt_pad = m.prompt_pad;
+  a.resp_pad = m.resp_pad;
+  a.branch_group = m.branch_group;
+  a.src_cu = m.src_cu;
+  a.items_tmp = m.tmp;
+  a.items = m.items;
+  a.cap = (int)cap;
+  a.tile_q = s.tile_q;
+  return launch_meta(a, st);
+}
+
+hipError_t run_transpose(const void* in, void* out, int heads, int hp, const Shape& s, int n_seg,
+                         const int32_t* seg_cu_d, const int32_t* seg_pad_d, long long pad_tokens,
+                         hipStream_t st) {
+  TransposeArgs t;
+  t.in = in;
+  t.out = out;
+  t.heads = heads;
+  t.hp = hp;
+  t.d = s.d;
+  t.n_seg = n_seg;
+  t.seg_cu = seg_cu_d;
+  t.seg_pad = seg_pad_d;
+  t.pad_tokens = (int)pad_tokens;
+  return launch_transpose(t, s.dtype, st);
+}
+
+}  // namespace
+
+namespace treeattn {
+void kernel_events(int kind, hipEvent_t* start, hipEvent_t* stop) {
+  *start = g_events[kind][0];
+  *stop = g_events[kind][1];
+}
+}  // namespace treeattn
+
+extern "C" {
+
+int tree_attn_workspace_size(const tree_attn_problem* problem, int op, size_t* bytes) {
+  if (!bytes) return TREE_ATTN_ERR_INVALID;
+  if (op < TREE_ATTN_OP_PREFILL || op > TREE_ATTN_OP_PREFILL_BWD) return TREE_ATTN_ERR_INVALID;
+  Shape s;
+  const int rc = validate_problem(problem, false, s);
+  if (rc != TREE_ATTN_OK) return rc;
+  *bytes = make_plan(s, op, nullptr).bytes;
+  return TREE_ATTN_OK;
+}
+
+int tree_attn_prefill(const tree_attn_problem* problem, const void* q_p, const void* k_p,
+                      const void* v_p, void* o_p, float* lse_p, void* ws, size_t ws_bytes,
+                      tree_attn_stream_t stream) {
+  Shape s;
+  int rc = validate_problem(problem, true, s);
+  if (rc != TREE_ATTN_OK) return rc;
+  for (const void* t : {q_p, k_p, v_p, static_cast<const void*>(o_p), static_cast<const void*>(lse_p)})
+    if (!tensor_ok(t, s.p_tokens)) return TREE_ATTN_ERR_INVALID;
+  Plan pl;
+  rc = check_ws(s, TREE_ATTN_OP_PREFILL, ws, ws_bytes, pl);
+  if (rc != TREE_ATTN_OK) return rc;
+  if (s.p_tokens == 0) return TREE_ATTN_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  TA_TRY(run_meta(problem, s, pl.mq, kMetaQPrefill, s.q_items_prefill, st));
+  TA_TRY(run_transpose(v_p, pl.vt_p, s.hkv, 1, s, s.ng, problem->prompt_cu_d, pl.mq.prompt_pad,
+                       s.p_pad, st));
+  FwdLaunch f;
+  f.q = q_p;
+  f.o = o_p;
+  f.lse = lse_p;
+  f.k_a = k_p;
+  f.vt_a = pl.vt_p;
+  f.k_b = k_p;
+  f.vt_b = pl.vt_p;
+  f.items = pl.mq.items;
+  f.n_items = (int)s.q_items_prefill;
+  f.hq = s.hq;
+  f.hkv = s.hkv;
+  f.hp = s.hp;
+  f.d = s.d;
+  f.dtype = s.dtype;
+  f.lse_stride = (int)s.p_tokens;
+  f.vt_a_stride = (int)s.p_pad;
+  f.vt_b_stride = (int)s.p_pad;
+  f.scale = problem->softmax_scale;
+  TA_TRY(launch_fwd(f, st));
+  return TREE_ATTN_OK;
+}
+
+int tree_attn_replay_fwd(const tree_attn_problem* problem, const void* k_p, const void* v_p,
+                         const void* q_r, const void* k_r, const void* v_r, void* o_r,
+                         float* lse_r, void* ws, size_t ws_bytes, tree_attn_stream_t stream) {
+  Shape s;
+  int rc = validate_problem(problem, true, s);
+  if (rc != TREE_ATTN_OK) return rc;
+  if (!tensor_ok(k_p, s.p_tokens) || !tensor_ok(v_p, s.p_tokens)) return TREE_ATTN_ERR_INVALID;
+  for (const void* t : {q_r, k_r, v_r, static_cast<const void*>(o_r), static_cast<const void*>(lse_r)})
+    if (!tensor_ok(t, s.r_tokens)) return TREE_ATTN_ERR_INVALID;
+  Plan pl;
+  rc = check_ws(s, TREE_ATTN_OP_REPLAY_FWD, ws, ws_bytes, pl);
+  if (rc != TREE_ATTN_OK) return rc;
+  if (s.r_tokens == 0) return TREE_ATTN_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  TA_TRY(run_meta(problem, s, pl.mq, kMetaQReplay, s.q_items_replay, st));
+  TA_TRY(run_transpose(v_p, pl.vt_p, s.hkv, 1, s, s.ng, problem->prompt_cu_d, pl.mq.prompt_pad,
+                       s.p_pad, st));
+  TA_TRY(run_transpose(v_r, pl.vt_r, s.hkv, 1, s, s.nb, problem->resp_cu_d, pl.mq.resp_pad,
+                       s.r_pad, st));
+  FwdLaunch f;
+  f.q = q_r;
+  f.o = o_r;
+  f.lse = lse_r;
+  f.k_a = k_p;
+  f.vt_a = pl.vt_p;
+  f.k_b = k_r;
+  f.vt_b = pl.vt_r;
+  f.items = pl.mq.items;
+  f.n_items = (int)s.q_items_replay;
+  f.hq = s.hq;
+  f.hkv = s.hkv;
+  f.hp = s.hp;
+  f.d = s.d;
+  f.dtype = s.dtype;
+  f.lse_stride = (int)s.r_tokens;
+  f.vt_a_stride = (int)s.p_pad;
+  f.vt_b_stride = (int)s.r_pad;
+  f.scale = problem->softmax_scale;
+  TA_TRY(launch_fwd(f, st));
+  return TREE_ATTN_OK;
+}
+
+int tree_attn_replay_bwd(const tree_attn_problem* problem, const void* k_p, const void* v_p,
+                         const void* q_r, const void* k_r, const void* v_r, const void* o_r,
+                         const float* lse_r, const void* do_r, void* dq_r, void* dk_r,
+                         void* dv_r, float* dk_p_seed, float* dv_p_seed, void* ws,
+                         size_t ws_bytes, tree_attn_stream_t stream) {
+  Shape s;
+  int rc = validate_problem(problem, true, s);
+  if (rc != TREE_ATTN_OK) return rc;
+  if ((dk_p_seed == nullptr) != (dv_p_seed == nullptr)) return TREE_ATTN_ERR_INVALID;
+  const bool seeds = dk_p_seed != nullptr;
+  if (!tensor_ok(k_p, s.p_tokens) || !tensor_ok(v_p, s.p_tokens)) return TREE_ATTN_ERR_INVALID;
+  if (seeds && (!tensor_ok(dk_p_seed, s.p_tokens) || !tensor_ok(dv_p_seed, s.p_tokens)))
+    return TREE_ATTN_ERR_INVALID;
+  for (const void* t : {q_r, k_r, v_r, o_r, static_cast<const void*>(lse_r), do_r,
+                        static_cast<const void*>(dq_r), static_cast<const void*>(dk_r),
+                        static_cast<const void*>(dv_r)})
+    if (!tensor_ok(t, s.r_tokens)) return TREE_ATTN_ERR_INVALID;
+  Plan pl;
+  rc = check_ws(s, TREE_ATTN_OP_REPLAY_BWD, ws, ws_bytes, pl);
+  if (rc != TREE_ATTN_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  // K-stationary list first: it also writes both padded offset arrays.
+  TA_TRY(run_meta(problem, s, pl.mk, kMetaKReplay, s.k_items_replay, st));
+  TA_TRY(run_meta(problem, s, pl.mq, kMetaQReplay, s.q_items_replay, st));
+  if (s.r_tokens > 0) {
+    TA_TRY(launch_row_dot(do_r, o_r, pl.delta, (int)s.r_tokens, s.hq, s.d, s.dtype, st));
+    TA_TRY(run_transpose(k_p, pl.kt_p, s.hkv, 1, s, s.ng, problem->prompt_cu_d,
+                         pl.mq.prompt_pad, s.p_pad, st));
+    TA_TRY(run_transpose(k_r, pl.kt_r, s.hkv, 1, s, s.nb, problem->resp_cu_d, pl.mq.resp_pad,
+                         s.r_pad, st));
+    TA_TRY(run_transpose(q_r, pl.qt, s.hq, s.hp, s, s.nb, problem->resp_cu_d, pl.mq.resp_pad,
+                         s.r_pad, st));
+    TA_TRY(run_transpose(do_r, pl.dot, s.hq, s.hp, s, s.nb, problem->resp_cu_d, pl.mq.resp_pad,
+                         s.r_pad, st));
+    DqLaunch q;
+    q.q = q_r;
+    q.dout = do_r;
+    q.lse = lse_r;
+    q.delta = pl.delta;
+    q.dq = dq_r;
+    q.k_a = k_p;
+    q.v_a = v_p;
+    q.kt_a = pl.kt_p;
+    q.k_b = k_r;
+    q.v_b = v_r;
+    q.kt_b = pl.kt_r;
+    q.items = pl.mq.items;
+    q.n_items = (int)s.q_items_replay;
+    q.hq = s.hq;
+    q.hkv = s.hkv;
+    q.hp = s.hp;
+    q.d = s.d;
+    q.dtype = s.dtype;
+    q.lse_stride = (int)s.r_tokens;
+    q.kt_a_stride = (int)s.p_pad;
+    q.kt_b_stride = (int)s.r_pad;
+    q.scale = problem->softmax_scale;
+    TA_TRY(launch_dq(q, st));
+  }
+  if (s.r_tokens > 0 || (seeds && s.p_tokens > 0)) {
+    DkvLaunch k;
+    k.k = k_r;
+    k.v = v_r;
+    k.k_prompt = k_p;
+    k.v_prompt = v_p;
+    k.q = q_r;
+    k.dout = do_r;
+    k.qt = pl.qt;
+    k.dot = pl.dot;
+    k.lse = lse_r;
+    k.delta = pl.delta;
+    k.seg_cu = problem->resp_cu_d;
+    k.seg_pad = pl.mk.resp_pad;
+    k.dk = dk_r;
+    k.dv = dv_r;
+    k.dk_seed = dk_p_seed;
+    k.dv_seed = dv_p_seed;
+    k.items = pl.mk.items;
+    k.n_items = (int)s.k_items_replay;
+    k.hq = s.hq;
+    k.hkv = s.hkv;
+    k.hp = s.hp;
+    k.d = s.d;
+    k.dtype = s.dtype;
+    k.lse_stride = (int)s.r_tokens;
+    k.qt_stride = (int)(s.r_pad * s.hp);
+    k.scale = problem->softmax_scale;
+    TA_TRY(launch_dkv(k, st));
+  }
+  return TREE_ATTN_OK;
+}
+
+int tree_attn_prefill_bwd(const tree_attn_problem* problem, const void* q_p, const void* k_p,
+                          const void* v_p, const void* o_p, const float* lse_p,
+                          const void* do_p, const float* dk_p_seed, const float* dv_p_seed,
+                          void* dq_p, void* dk_p, void* dv_p, void* ws, size_t ws_bytes,
+                          tree_attn_stream_t stream) {
+  Shape s;
+  int rc = validate_problem(problem, true, s);
+  if (rc != TREE_ATTN_OK) return rc;
+  if ((dk_p_seed == nullptr) != (dv_p_seed == nullptr)) return TREE_ATTN_ERR_INVALID;
+  for (const void* t : {q_p, k_p, v_p, o_p, static_cast<const void*>(lse_p), do_p,
+                        static_cast<const void*>(dq_p), static_cast<const void*>(dk_p),
+                        static_cast<const void*>(dv_p)})
+    if (!tensor_ok(t, s.p_tokens)) return TREE_ATTN_ERR_INVALID;
+  if (dk_p_seed && (!tensor_ok(dk_p_seed, s.p_tokens) || !tensor_ok(dv_p_seed, s.p_tokens)))
+    return TREE_ATTN_ERR_INVALID;
+  Plan pl;
+  rc = check_ws(s, TREE_ATTN_OP_PREFILL_BWD, ws, ws_bytes, pl);
+  if (rc != TREE_ATTN_OK) return rc;
+  if (s.p_tokens == 0) return TREE_ATTN_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  TA_TRY(run_meta(problem, s, pl.mk, kMetaKPrefill, s.k_items_prefill, st));
+  TA_TRY(run_meta(problem, s, pl.mq, kMetaQPrefill, s.q_items_prefill, st));
+  TA_TRY(launch_row_dot(do_p, o_p, pl.delta, (int)s.p_tokens, s.hq, s.d, s.dtype, st));
+  TA_TRY(run_transpose(k_p, pl.kt_p, s.hkv, 1, s, s.ng, problem->prompt_cu_d, pl.mq.prompt_pad,
+                       s.p_pad, st));
+  TA_TRY(run_transpose(q_p, pl.qt, s.hq, s.hp, s, s.ng, problem->prompt_cu_d, pl.mq.prompt_pad,
+                       s.p_pad, st));
+  TA_TRY(run_transpose(do_p, pl.dot, s.hq, s.hp, s, s.ng, problem->prompt_cu_d,
+                       pl.mq.prompt_pad, s.p_pad, st));
+  DqLaunch q;
+  q.q = q_p;
+  q.dout = do_p;
+  q.lse = lse_p;
+  q.delta = pl.delta;
+  q.dq = dq_p;
+  q.k_a = k_p;
+  q.v_a = v_p;
+  q.kt_a = pl.kt_p;
+  q.k_b = k_p;
+  q.v_b = v_p;
+  q.kt_b = pl.kt_p;
+  q.items = pl.mq.items;
+  q.n_items = (int)s.q_items_prefill;
+  q.hq = s.hq;
+  q.hkv = s.hkv;
+  q.hp = s.hp;
+  q.d = s.d;
+  q.dtype = s.dtype;
+  q.lse_stride = (int)s.p_tokens;
+  q.kt_a_stride = (int)s.p_pad;
+  q.kt_b_stride = (int)s.p_pad;
+  q.scale = problem->softmax_scale;
+  TA_TRY(launch_dq(q, st));
+  DkvLaunch k;
+  k.k = k_p;
+  k.v = v_p;
+  k.k_prompt = k_p;
+  k.v_prompt = v_p;
+  k.q = q_p;
+  k.dout = do_p;
+  k.qt = pl.qt;
+  k.dot = pl.dot;
+  k.lse = lse_p;
+  k.delta = pl.delta;
+  k.seg_cu = problem->prompt_cu_d;
+  k.seg_pad = pl.mk.prompt_pad;
+  k.dk = dk_p;
+  k.dv = dv_p;
+  k.dk_seed = const_cast<float*>(dk_p_seed);
+  k.dv_seed = const_cast<float*>(dv_p_seed);
+  k.items = pl.mk.items;
+  k.n_items = (int)s.k_items_prefill;
+  k.hq = s.hq;
+  k.hkv = s.hkv;
+  k.hp = s.hp;
+  k.d = s.d;
+  k.dtype = s.dtype;
+  k.lse_stride = (int)s.p_tokens;
+  k.qt_stride = (int)(s.p_pad * s.hp);
+  k.scale = problem->softmax_scale;
+  TA_TRY(launch_dkv(k, st));
+  return TREE_ATTN_OK;
+}
+
+int lse_merge(int32_t num_splits, int32_t rows, int32_t heads, int32_t head_dim,
+              int32_t out_dtype, const float* o_parts, const float* lse_parts, void* o_out,
+              float* lse_out, tree_attn_stream_t stream) {
+  if (out_dtype != TREE_ATTN_F32 && out_dtype != TREE_ATTN_BF16) return TREE_ATTN_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return TREE_ATTN_ERR_UNSUPPORTED;
+  if (num_splits < 1 || rows < 0 || heads < 1) return TREE_ATTN_ERR_INVALID;
+  if ((long long)num_splits * rows * heads * head_dim > (1LL << 40)) return TREE_ATTN_ERR_INVALID;
+  if (rows > 0 && (!o_parts || !lse_parts || !o_out || !lse_out)) return TREE_ATTN_ERR_INVALID;
+  if (rows == 0) return TREE_ATTN_OK;
+  (void)hipGetLastError();
+  TA_TRY(launch_lse_merge(num_splits, rows, heads, head_dim, out_dtype, o_parts, lse_parts, o_out,
+                          lse_out, static_cast<hipStream_t>(stream)));
+  return TREE_ATTN_OK;
+}
+
+int tree_attn_set_kernel_events(int kind, void* start_event, void* stop_event) {
+  if (kind < 0 || kind > 2) return TREE_ATTN_ERR_INVALID;
+  if ((start_event == nullptr) != (stop_event == nullptr)) return TREE_ATTN_ERR_INVALID;
+  g_events[kind][0] = static_cast<hipEvent_t>(start_event);
+  g_events[kind][1] = static_cast<hipEvent_t>(stop_event);
+  return TREE_ATTN_OK;
+}
+
+int tree_attn_last_hip_error(void) { return static_cast<int>(g_last_hip); }
+
+const char* tree_attn_error_string(int code) {
+  switch (code) {
+    case TREE_ATTN_OK: return "ok";
+    case TREE_ATTN_ERR_INVALID: return "invalid argument";
+    case TREE_ATTN_ERR_UNSUPPORTED: return "unsupported dtype or head_dim";
+    case TREE_ATTN_ERR_WORKSPACE: return "workspace too small";
+    case TREE_ATTN_ERR_HIP: return "HIP launch or runtime error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,121 @@
+"""The C ABI library without a GPU: it loads, exports every entry point the
+header declares, sizes workspaces, and rejects bad arguments on the host
+before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+from shared_prompt_tree_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tree_attn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(ops.LIB_PATH),
+                                reason="libtreeattn.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"tree_attn_prefill", "tree_attn_replay_fwd", "tree_attn_replay_bwd",
+            "tree_attn_prefill_bwd", "lse_merge", "tree_attn_workspace_size",
+            "tree_attn_error_string"} <= set(names)
+    lib = ops.library()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_error_strings():
+    lib = ops.library()
+    for code in (0, -1, -2, -3, -4, 7):
+        assert lib.tree_attn_error_string(code)
+
+
+def small_problem(**kw):
+    args = dict(prompt_cu=[0, 5, 9], group_branch_cu=[0, 2, 3], resp_cu=[0, 3, 3, 7],
+                num_q_heads=4, num_kv_heads=2, head_dim=128, dtype=torch.bfloat16)
+    args.update(kw)
+    return ops.TreeProblem(**args)
+
+
+def test_workspace_sizes_grow_with_tokens():
+    a = small_problem()
+    b = small_problem(prompt_cu=[0, 500, 900], resp_cu=[0, 300, 300, 700])
+    for op in range(4):
+        assert 0 < ops.tree_attn_workspace_size(a, op) < ops.tree_attn_workspace_size(b, op)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=96), -2),
+    (dict(dtype=torch.float16), -2),
+    (dict(num_kv_heads=3), -1),
+    (dict(prompt_cu=[1, 5, 9]), -1),
+    (dict(prompt_cu=[0, 5, 4]), -1),
+    (dict(group_branch_cu=[0, 2, 2]), -1),
+    (dict(resp_cu=[0, 3, 2, 7]), -1),
+    (dict(softmax_scale=0.0), -1),
+    (dict(softmax_scale=float("nan")), -1),
+])
+def test_invalid_problem_rejected(kw, code):
+    p = small_problem(**kw)
+    with pytest.raises(ops.TreeAttnError) as e:
+        ops.tree_attn_workspace_size(p, ops.OP_PREFILL)
+    assert e.value.code == code
+
+
+def test_bad_op_and_null_out_pointer():
+    lib = ops.library()
+    p = small_problem()
+    n = ctypes.c_size_t(0)
+    assert lib.tree_attn_workspace_size(ctypes.byref(p.c), 9, ctypes.byref(n)) == -1
+    assert lib.tree_attn_workspace_size(ctypes.byref(p.c), 0, None) == -1
+    assert lib.tree_attn_workspace_size(None, 0, ctypes.byref(n)) == -1
+
+
+def test_entry_points_reject_before_any_hip_call():
+    """Missing device offsets, null tensors, misaligned tensors, a single
+    seed pointer and a short workspace are all refused on the host."""
+    lib = ops.library()
+    p = small_problem()  # no device arrays
+    vp = ctypes.c_void_p
+    fake = vp(1 << 20)  # never dereferenced: validation fails first
+    assert lib.tree_attn_prefill(ctypes.byref(p.c), fake, fake, fake, fake, fake, fake,
+                                 1 << 30, None) == -1
+    # device offsets present (fake addresses), null q
+    p.c.prompt_cu_d = p.c.group_branch_cu_d = p.c.resp_cu_d = 1 << 20
+    assert lib.tree_attn_prefill(ctypes.byref(p.c), None, fake, fake, fake, fake, fake,
+                                 1 << 30, None) == -1
+    # misaligned tensor
+    assert lib.tree_attn_prefill(ctypes.byref(p.c), vp((1 << 20) + 2), fake, fake, fake, fake,
+                                 fake, 1 << 30, None) == -1
+    # workspace too small
+    assert lib.tree_attn_prefill(ctypes.byref(p.c), fake, fake, fake, fake, fake, fake, 16,
+                                 None) == -3
+    # exactly one seed pointer
+    assert lib.tree_attn_replay_bwd(ctypes.byref(p.c), *([fake] * 11), fake, None, fake,
+                                    1 << 30, None) == -1
+    assert lib.tree_attn_prefill_bwd(ctypes.byref(p.c), *([fake] * 6), None, fake, fake, fake,
+                                     fake, fake, 1 << 30, None) == -1
+    # lse_merge argument checks
+    assert lib.lse_merge(0, 4, 2, 128, 1, fake, fake, fake, fake, None) == -1
+    assert lib.lse_merge(2, 4, 2, 80, 1, fake, fake, fake, fake, None) == -2
+    assert lib.lse_merge(2, 4, 2, 128, 5, fake, fake, fake, fake, None) == -2
+    assert lib.lse_merge(2, 4, 2, 128, 1, None, fake, fake, fake, None) == -1
+    assert lib.lse_merge(2, 0, 2, 128, 1, None, None, None, None, None) == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(ops, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(ops, "_lib", None)
+    with pytest.raises(RuntimeError, match="not found"):
+        ops.library()

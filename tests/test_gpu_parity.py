@@ -1,0 +1,132 @@
+"""HIP library vs the float64 oracle, element by element (GPU).
+
+Every case runs the whole path (prefill, replay forward, replay backward
+with seeds, prefill backward) through the C ABI and compares all ten outputs
+by relative L2: 1e-5 for float32, 1e-2 for bf16.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from shared_prompt_tree_amd import ops
+from shared_prompt_tree_amd import workloads as wl
+from tests._gpu import (TOL, compare, host64, make_case, oracle_inputs, rel_l2, run_library,
+                        run_oracle, say)
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(tree, seed, value_scale=1.0, label="", zero_do_p=False):
+    say(f"[case] {label} groups={tree.n_groups} hq={tree.hq} hkv={tree.hkv} d={tree.d} "
+        f"dtype={tree.dtype} P={tree.prompt_lens} r={tree.resp_lens}")
+    prob, t = make_case(tree, seed, value_scale, zero_do_p)
+    lib = run_library(prob, t)
+    ref = run_oracle(tree, t)
+    return prob, t, lib, ref
+
+
+def test_tiny_f32_full():
+    spec = wl.SPECS["tiny"]
+    tree = wl.make_tree(spec)
+    _, _, lib, ref = _case(tree, spec.seed, spec.value_scale, "tiny")
+    compare(lib, ref, TOL["f32"], label="tiny")
+
+
+def test_small_bf16_full():
+    spec = wl.SPECS["small"]
+    tree = wl.make_tree(spec)
+    _, _, lib, ref = _case(tree, spec.seed, 1.0, "small")
+    compare(lib, ref, TOL["bf16"], label="small")
+
+
+# Oracle-sized versions of the large shapes: the same heads, head_dim and
+# length mix, fewer and shorter sequences, lengths that are not tile
+# multiples.
+REDUCED = {
+    "prompt_heavy": wl.Tree([4097], [[300, 511, 64, 1]], 32, 8, 128, "bf16"),
+    "response_heavy": wl.Tree([256, 130], [[1500, 777, 2049], [1030, 3]], 32, 8, 128, "bf16"),
+    "long_mixed": wl.Tree([6000], [[1024, 1900, 3500]], 32, 8, 128, "bf16"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(REDUCED))
+def test_reduced_shapes_full(name):
+    tree = REDUCED[name]
+    _, _, lib, ref = _case(tree, 7, 1.0, name)
+    compare(lib, ref, TOL["bf16"], label=name)
+
+
+EDGE = {
+    "one-token prompt": wl.Tree([1], [[70, 5]], 4, 2, 128, "bf16"),
+    "single branch": wl.Tree([333], [[129]], 8, 2, 128, "bf16"),
+    "empty branches": wl.Tree([200, 77], [[0, 65, 0], [0]], 4, 1, 128, "bf16"),
+    "group without branches": wl.Tree([90, 150], [[], [40, 300]], 4, 4, 128, "bf16"),
+    "empty prompt": wl.Tree([0, 64], [[31, 200], [7]], 4, 2, 128, "bf16"),
+    "MHA head_dim 64": wl.Tree([300], [[100, 257]], 3, 3, 64, "bf16"),
+    "GQA 7:1 (Qwen2.5-7B grouping)": wl.Tree([260], [[90, 130]], 14, 2, 128, "bf16"),
+    "MQA": wl.Tree([129], [[64, 65]], 8, 1, 128, "bf16"),
+    "f32 head_dim 128": wl.Tree([150], [[40, 90]], 2, 1, 128, "f32"),
+    "f32 GQA ragged": wl.Tree([70, 33], [[5, 64, 1], [100]], 4, 2, 64, "f32"),
+}
+
+
+@pytest.mark.parametrize("name", list(EDGE))
+def test_edge_cases(name):
+    tree = EDGE[name]
+    vs = 0.125 if tree.dtype == "f32" else 1.0
+    _, _, lib, ref = _case(tree, 11, vs, name)
+    compare(lib, ref, TOL[tree.dtype], label=name)
+
+
+def test_zero_prompt_upstream_gradient():
+    """dO_P = 0: dQ_P must be exactly zero; everything else still matches."""
+    tree = wl.Tree([500], [[200, 64]], 8, 2, 128, "bf16")
+    _, _, lib, ref = _case(tree, 5, 1.0, "dO_P=0", zero_do_p=True)
+    assert float(lib["dq_p"].abs().max()) == 0.0
+    names = [n for n in ("o_p", "lse_p", "o_r", "lse_r", "dk_p", "dv_p", "dq_r", "dk_r", "dv_r")]
+    compare(lib, ref, TOL["bf16"], names=names, label="dO_P=0")
+
+
+def test_detached_prompt_seeds():
+    """With no seeds, prefill backward returns only the prompt rows' own
+    term, i.e. the gradients of a tree whose groups have no branch."""
+    tree = wl.Tree([300, 129], [[100, 64], [50]], 4, 2, 128, "bf16")
+    prob, t = make_case(tree, 9)
+    lib = run_library(prob, t, seeds=False)
+    prompt_only = wl.Tree(tree.prompt_lens, [[] for _ in tree.prompt_lens], 4, 2, 128, "bf16")
+    ti = {k: v for k, v in t.items() if k.endswith("_p")}
+    for k in ("q_r", "k_r", "v_r", "do_r"):
+        ti[k] = t[k][:0]
+    ref = run_oracle(prompt_only, ti)
+    compare(lib, ref, TOL["bf16"], names=("dq_p", "dk_p", "dv_p"), label="detached")
+
+
+def test_deterministic():
+    """No atomics on any output: two runs are bit-identical."""
+    tree = wl.Tree([700], [[300, 129, 64]], 8, 2, 128, "bf16")
+    prob, t = make_case(tree, 3)
+    a = run_library(prob, t)
+    b = run_library(prob, t)
+    for k, v in a.items():
+        if v is not None:
+            assert torch.equal(v, b[k]), k
+
+
+def test_lse_merge_matches_oracle():
+    import oracle
+    g = torch.Generator(device="cuda").manual_seed(4)
+    S, rows, H, d = 5, 333, 6, 128
+    o = torch.randn(S, rows, H, d, device="cuda", generator=g)
+    lse = torch.randn(S, H, rows, device="cuda", generator=g) * 4
+    lse[1, :, :50] = float("-inf")  # empty parts
+    lse[:, 2, 7] = float("-inf")    # a row where every part is empty
+    for dt, tol in ((torch.float32, 1e-6), (torch.bfloat16, 1e-2)):
+        mo, ml = ops.lse_merge(o, lse, out_dtype=dt)
+        torch.cuda.synchronize()
+        ro, rl = oracle.lse_merge(host64(o), host64(lse))
+        assert float(mo[7, 2].abs().max()) == 0.0 and float(ml[2, 7]) == float("-inf")
+        fin = np.isfinite(rl)
+        assert np.array_equal(np.isfinite(host64(ml)), fin)
+        assert rel_l2(host64(ml)[fin], rl[fin]) < 1e-6
+        assert rel_l2(host64(mo), ro) < tol
