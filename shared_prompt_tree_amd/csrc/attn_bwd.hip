@@ -4,8 +4,8 @@
 // With P = exp(scale * Q K^T - LSE), D = rowsum(dO * O), dP = dO V^T and
 // dS = P * (dP - D):  dQ = scale * dS K,  dK = scale * dS^T Q,  dV = P^T dO.
 //
-// dkv_kernel is key-stationary.  A workgroup (4 waves x 32 keys) owns 128 keys
-// of one kv head, keeps their K and V in registers, and loops over every
+// dkv_kernel is key-stationary.  A workgroup (8 waves x 32 keys) owns 256 keys
+// of one kv head, keeps them on chip, and loops over every
 // query row that reads them, for all query heads of that kv head.  For a
 // prompt tile in replay that is every response row of every branch of the
 // group, so the sum over branches of Eq. 2 happens in the accumulators and
@@ -54,9 +54,9 @@ template <typename T, int D, int KB>
 __global__ __launch_bounds__(512) void dq_kernel(DqArgs<T, D> a) {
   constexpr int NT = 512, KT = 32 * KB, CH = ChunkOf<T>::kElems;
   constexpr int NCHK = D / CH, NCHT = KT / CH;
-  constexpr int KTILE = KT * D;
-  constexpr int KCH = KT * NCHK, TCH = D * NCHT;
-  constexpr int KPER = (KCH + NT - 1) / NT, TPER = (TCH + NT - 1) / NT;
+  constexpr int KROW = tile_row_elems<T, NCHK>(), TROW = tile_row_elems<T, NCHT>();
+  constexpr int KTILE = tile_elems<T, KT, NCHK>();  // K or V tile (with slack)
+  constexpr int STAGE = 2 * KTILE + tile_elems<T, D, NCHT>();
   constexpr int NKK = D / 16, NDB = D / 32;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   T* smem = reinterpret_cast<T*>(smem_raw);
@@ -100,64 +100,23 @@ __global__ __launch_bounds__(512) void dq_kernel(DqArgs<T, D> a) {
   const int total = na + nb;
   const size_t kv_stride = (size_t)a.hkv * D;
 
-  u32x4 kst[KPER], vst[KPER], tst[TPER];
+  // Tile j into LDS stage j % 2: K and V rows (keys past the segment are
+  // clamped to its last key and masked later) and K^T rows (padded copy).
   auto gload = [&](int j) {
     const bool inA = j < na;
     const int ks = (inA ? j : j - na) * KT;
-    const size_t base = (size_t)(inA ? it.a0 : it.b0) * kv_stride;
+    const size_t base = (size_t)((inA ? it.a0 : it.b0) + ks) * kv_stride + kv * D;
     const T* kb = (inA ? a.k_a : a.k_b) + base;
     const T* vb = (inA ? a.v_a : a.v_b) + base;
-    const int klen = inA ? it.alen : it.blen;
-#pragma unroll
-    for (int i = 0; i < KPER; ++i) {
-      const int qi = tid + NT * i;
-      if (KCH % NT == 0 || qi < KCH) {
-        const int r = qi / NCHK, c = qi % NCHK;
-        const int key = ks + r;
-        if (key < klen) {
-          const size_t o = (size_t)key * kv_stride + kv * D + c * CH;
-          kst[i] = *reinterpret_cast<const u32x4*>(kb + o);
-          vst[i] = *reinterpret_cast<const u32x4*>(vb + o);
-        } else {
-          kst[i] = u32x4{0, 0, 0, 0};
-          vst[i] = u32x4{0, 0, 0, 0};
-        }
-      }
-    }
+    const int klast = (inA ? it.alen : it.blen) - 1 - ks;
     const int tstride = inA ? a.kt_a_stride : a.kt_b_stride;
     const T* tb = (inA ? a.kt_a + (size_t)kv * D * a.kt_a_stride + it.apad
                        : a.kt_b + (size_t)kv * D * a.kt_b_stride + it.bpad) + ks;
-#pragma unroll
-    for (int i = 0; i < TPER; ++i) {
-      const int qi = tid + NT * i;
-      if (TCH % NT == 0 || qi < TCH) {
-        const int dd = qi / NCHT, c = qi % NCHT;
-        tst[i] = *reinterpret_cast<const u32x4*>(tb + (size_t)dd * tstride + c * CH);
-      }
-    }
-  };
-  auto lstore = [&](int stage) {
-    T* ks_ = smem + stage * 3 * KTILE;
-    T* vs_ = ks_ + KTILE;
-    T* ts_ = vs_ + KTILE;
-#pragma unroll
-    for (int i = 0; i < KPER; ++i) {
-      const int qi = tid + NT * i;
-      if (KCH % NT == 0 || qi < KCH) {
-        const int r = qi / NCHK, c = qi % NCHK;
-        const int o = r * D + ((c ^ swz_row<NCHK>(r)) * CH);
-        *reinterpret_cast<u32x4*>(ks_ + o) = kst[i];
-        *reinterpret_cast<u32x4*>(vs_ + o) = vst[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < TPER; ++i) {
-      const int qi = tid + NT * i;
-      if (TCH % NT == 0 || qi < TCH) {
-        const int dd = qi / NCHT, c = qi % NCHT;
-        *reinterpret_cast<u32x4*>(ts_ + dd * KT + ((c ^ swz_row<NCHT>(dd)) * CH)) = tst[i];
-      }
-    }
+    T* ks_ = smem + (j & 1) * STAGE;
+    auto krow = [&](int r) { return min(r, klast) * (int)kv_stride; };
+    g2l_tile<T, KT, NCHK, NT>(ks_, kb, krow);
+    g2l_tile<T, KT, NCHK, NT>(ks_ + KTILE, vb, krow);
+    g2l_tile<T, D, NCHT, NT>(ks_ + 2 * KTILE, tb, [&](int r) { return r * tstride; });
   };
 
   f32x16 acc[NDB];
@@ -166,14 +125,12 @@ __global__ __launch_bounds__(512) void dq_kernel(DqArgs<T, D> a) {
   const float c2 = a.scale_log2;
   const int wave_tok0 = (32 * w) / a.hp;
 
-  if (total > 0) {
-    gload(0);
-    lstore(0);
-  }
+  if (total > 0) gload(0);
+  wait_vmem();
   __syncthreads();
   for (int j = 0; j < total; ++j) {
     if (j + 1 < total) gload(j + 1);
-    const T* ks_ = smem + (j & 1) * 3 * KTILE;
+    const T* ks_ = smem + (j & 1) * STAGE;
     const T* vs_ = ks_ + KTILE;
     const T* ts_ = vs_ + KTILE;
 
@@ -186,8 +143,8 @@ __global__ __launch_bounds__(512) void dq_kernel(DqArgs<T, D> a) {
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         Frag<T> kf, vf;
-        lds_frag(kf, ks_, kr, D, 16 * kk + 8 * lh, swz_row<NCHK>(kr));
-        lds_frag(vf, vs_, kr, D, 16 * kk + 8 * lh, swz_row<NCHK>(kr));
+        lds_frag(kf, ks_, kr, KROW, 16 * kk + 8 * lh);
+        lds_frag(vf, vs_, kr, KROW, 16 * kk + 8 * lh);
         mma(s[kb], kf, qf[kk]);
         mma(dp[kb], vf, gf[kk]);
       }
@@ -220,11 +177,11 @@ __global__ __launch_bounds__(512) void dq_kernel(DqArgs<T, D> a) {
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
           Frag<T> tf;
-          lds_frag(tf, ts_, tr, KT, 16 * (2 * kb + hf) + 8 * lh, swz_row<NCHT>(tr));
+          lds_frag(tf, ts_, tr, TROW, 16 * (2 * kb + hf) + 8 * lh);
           mma(acc[db], tf, sf[kb][hf]);
         }
     }
-    if (j + 1 < total) lstore((j + 1) & 1);
+    wait_vmem();
     __syncthreads();
   }
 
@@ -276,18 +233,28 @@ struct DkvArgs {
   float scale_log2, scale;
 };
 
+// Key-stationary dK/dV.  A workgroup of NW = 8 waves owns 32 * NW keys of one
+// kv head; wave w owns keys [32w, 32w + 32).  With two waves per SIMD the
+// MFMA phase of one wave overlaps the exponentials of the other.  V of the
+// wave's keys stays in registers; for bf16 the K tile stays in LDS for the
+// whole loop (registers would not fit two waves per SIMD), for float32 K
+// stays in registers.  Query blocks of 32 rows (Q, dO, Q^T, dO^T, LSE, D)
+// stream through LDS, double buffered.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void dkv_kernel(DkvArgs<T, D> a) {
-  constexpr int NT = 256, QB = 32, CH = ChunkOf<T>::kElems;
+__global__ __launch_bounds__(512) void dkv_kernel(DkvArgs<T, D> a) {
+  constexpr int NW = 8, NT = 64 * NW, QB = 32, CH = ChunkOf<T>::kElems;
+  constexpr bool KLDS = sizeof(T) == 2;
   constexpr int NCHQ = D / CH, NCHT = QB / CH;
-  constexpr int QTILE = QB * D;                   // elements per staged tensor
-  constexpr int STAGE = 4 * QTILE;                // Q, dO, Q^T, dO^T
-  constexpr int QCH = QB * NCHQ, TCH = D * NCHT;  // chunks per tensor
-  constexpr int QPER = (QCH + NT - 1) / NT, TPER = (TCH + NT - 1) / NT;
+  constexpr int QROW = tile_row_elems<T, NCHQ>(), TROW = tile_row_elems<T, NCHT>();
+  constexpr int QTILE = tile_elems<T, QB, NCHQ>();  // Q or dO block
+  constexpr int TTILE = tile_elems<T, D, NCHT>();   // Q^T or dO^T block
+  constexpr int STAGE = 2 * QTILE + 2 * TTILE;      // Q, dO, Q^T, dO^T
+  constexpr int KTILE = KLDS ? tile_elems<T, 32 * NW, NCHQ>() : 0;  // resident K tile
   constexpr int NKK = D / 16, NDB = D / 32;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   T* smem = reinterpret_cast<T*>(smem_raw);
-  float* fsm = reinterpret_cast<float*>(smem + 2 * STAGE);  // [2][2][QB] lse2, delta
+  T* ktile = smem + 2 * STAGE;
+  float* fsm = reinterpret_cast<float*>(ktile + KTILE);  // [2][2][QB] lse2, delta
 
   int item_idx, kv;
   if (!xcd_map(blockIdx.x, a.n_items, a.hkv, item_idx, kv)) return;
@@ -303,22 +270,27 @@ __global__ __launch_bounds__(256) void dkv_kernel(DkvArgs<T, D> a) {
   const int tpb = QB / hp;  // query tokens per block
   const size_t kv_stride = (size_t)a.hkv * D;
 
-  // K and V of this lane's key (operand row = key), kept for the whole loop.
-  Frag<T> kf[NKK], vf[NKK];
+  // V (and for float32 also K) of this lane's key, kept for the whole loop.
+  Frag<T> vf[NKK];
+  Frag<T> kf[KLDS ? 1 : NKK];
   {
     const int key = 32 * w + lr;
     const bool ok = key < it.nk;
     const size_t off = (size_t)(it.k0 + (ok ? key : 0)) * kv_stride + kv * D;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      if (ok) {
-        load_frag(kf[kk], ksrc + off + 16 * kk + 8 * lh);
-        load_frag(vf[kk], vsrc + off + 16 * kk + 8 * lh);
-      } else {
-        kf[kk].v = {};
-        vf[kk].v = {};
+      if (ok) load_frag(vf[kk], vsrc + off + 16 * kk + 8 * lh);
+      else vf[kk].v = {};
+      if constexpr (!KLDS) {
+        if (ok) load_frag(kf[kk], ksrc + off + 16 * kk + 8 * lh);
+        else kf[kk].v = {};
       }
     }
+  }
+  if constexpr (KLDS) {
+    // resident K tile [32*NW keys][D]; keys past the tile end are clamped
+    const T* kb = ksrc + (size_t)it.k0 * kv_stride + kv * D;
+    g2l_tile<T, 32 * NW, NCHQ, NT>(ktile, kb, [&](int r) { return min(r, it.nk - 1) * (int)kv_stride; });
   }
 
   // Query block cursor: head sub-group hs, segment seg, block blk.
@@ -347,38 +319,24 @@ __global__ __launch_bounds__(256) void dkv_kernel(DkvArgs<T, D> a) {
     }
   };
 
-  u32x4 qst[QPER], gst[QPER], tqst[TPER], tgst[TPER];
+  // Query block -> LDS stage: Q and dO rows (tokens past the segment are
+  // clamped to its last token; their LSE is +inf so they add nothing), Q^T
+  // and dO^T rows (padded copies), and LSE*log2(e) and D through registers.
   float lst = 0.f;
-  auto gload = [&](const Cur& c) {
+  auto gload = [&](const Cur& c, int stage) {
     const int hg = kv * a.nsub + c.hs;
     const int tok0 = c.blk * tpb;
-#pragma unroll
-    for (int i = 0; i < QPER; ++i) {
-      const int qi = tid + NT * i;
-      if (QCH % NT == 0 || qi < QCH) {
-        const int r = qi / NCHQ, ch = qi % NCHQ;
-        const int tok = tok0 + r / hp;
-        if (tok < c.nq) {
-          const size_t o = ((size_t)(c.q0 + tok) * a.hq + hg * hp + (r % hp)) * D + ch * CH;
-          qst[i] = *reinterpret_cast<const u32x4*>(a.q + o);
-          gst[i] = *reinterpret_cast<const u32x4*>(a.dout + o);
-        } else {
-          qst[i] = u32x4{0, 0, 0, 0};
-          gst[i] = u32x4{0, 0, 0, 0};
-        }
-      }
-    }
+    const int last = c.nq - 1;
+    T* qs = smem + stage * STAGE;
+    const size_t qoff = ((size_t)(c.q0 + tok0) * a.hq + (size_t)hg * hp) * D;
+    const int rows_left = last - tok0;
+    auto qrow = [&](int r) { return min(r / hp, rows_left) * a.hq * D + (r % hp) * D; };
+    g2l_tile<T, QB, NCHQ, NT>(qs, a.q + qoff, qrow);
+    g2l_tile<T, QB, NCHQ, NT>(qs + QTILE, a.dout + qoff, qrow);
     const size_t tb = (size_t)hg * D * a.qt_stride + (size_t)c.qpad * hp + (size_t)c.blk * QB;
-#pragma unroll
-    for (int i = 0; i < TPER; ++i) {
-      const int qi = tid + NT * i;
-      if (TCH % NT == 0 || qi < TCH) {
-        const int dd = qi / NCHT, ch = qi % NCHT;
-        const size_t o = tb + (size_t)dd * a.qt_stride + ch * CH;
-        tqst[i] = *reinterpret_cast<const u32x4*>(a.qt + o);
-        tgst[i] = *reinterpret_cast<const u32x4*>(a.dot + o);
-      }
-    }
+    auto trow = [&](int r) { return r * a.qt_stride; };
+    g2l_tile<T, D, NCHT, NT>(qs + 2 * QTILE, a.qt + tb, trow);
+    g2l_tile<T, D, NCHT, NT>(qs + 2 * QTILE + TTILE, a.dot + tb, trow);
     if (tid < 2 * QB) {
       const int r = tid & (QB - 1);
       const int tok = tok0 + r / hp;
@@ -388,30 +346,6 @@ __global__ __launch_bounds__(256) void dkv_kernel(DkvArgs<T, D> a) {
     }
   };
   auto lstore = [&](int stage) {
-    T* qs = smem + stage * STAGE;
-    T* gs = qs + QTILE;
-    T* tqs = gs + QTILE;
-    T* tgs = tqs + QTILE;
-#pragma unroll
-    for (int i = 0; i < QPER; ++i) {
-      const int qi = tid + NT * i;
-      if (QCH % NT == 0 || qi < QCH) {
-        const int r = qi / NCHQ, ch = qi % NCHQ;
-        const int o = r * D + ((ch ^ swz_row<NCHQ>(r)) * CH);
-        *reinterpret_cast<u32x4*>(qs + o) = qst[i];
-        *reinterpret_cast<u32x4*>(gs + o) = gst[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < TPER; ++i) {
-      const int qi = tid + NT * i;
-      if (TCH % NT == 0 || qi < TCH) {
-        const int dd = qi / NCHT, ch = qi % NCHT;
-        const int o = dd * QB + ((ch ^ swz_row<NCHT>(dd)) * CH);
-        *reinterpret_cast<u32x4*>(tqs + o) = tqst[i];
-        *reinterpret_cast<u32x4*>(tgs + o) = tgst[i];
-      }
-    }
     if (tid < 2 * QB) fsm[stage * 2 * QB + tid] = lst;
   };
 
@@ -422,8 +356,11 @@ __global__ __launch_bounds__(256) void dkv_kernel(DkvArgs<T, D> a) {
     dva[db] = f32x16{};
   }
   const float c2 = a.scale_log2;
-  const int key_loc = it.kpos + 32 * w + lr;    // this lane's key, segment position
-  const int wave_kmax = it.kpos + 32 * w + 31;  // largest key position of the wave
+  const int key_loc = it.kpos + 32 * w + lr;  // this lane's key, segment position
+  const int wave_kmin = it.kpos + 32 * w;     // smallest key position of the wave
+  const int wave_kmax = wave_kmin + 31;
+  const bool wave_has_keys = 32 * w < it.nk;
+  const int krow = 32 * w + lr;               // this lane's row of the K tile
 
   Cur cur{0, it.seg_lo, 0, 0, 0, 0, 0};
   bool have = false;
@@ -432,68 +369,79 @@ __global__ __launch_bounds__(256) void dkv_kernel(DkvArgs<T, D> a) {
     have = settle(cur);
   }
   if (have) {
-    gload(cur);
+    gload(cur, 0);
     lstore(0);
   }
+  wait_vmem();
   __syncthreads();
   int stage = 0;
   while (have) {
     Cur nxt = cur;
     ++nxt.blk;
     const bool more = settle(nxt);
-    if (more) gload(nxt);
+    if (more) gload(nxt, stage ^ 1);
     const T* qs = smem + stage * STAGE;
     const T* gs = qs + QTILE;
     const T* tqs = gs + QTILE;
-    const T* tgs = tqs + QTILE;
+    const T* tgs = tqs + TTILE;
     const float* lse_s = fsm + stage * 2 * QB;
     const float* del_s = lse_s + QB;
-
-    f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      Frag<T> qa, ga;
-      lds_frag(qa, qs, lr, D, 16 * kk + 8 * lh, swz_row<NCHQ>(lr));
-      lds_frag(ga, gs, lr, D, 16 * kk + 8 * lh, swz_row<NCHQ>(lr));
-      mma(s, qa, kf[kk]);
-      mma(dp, ga, vf[kk]);
-    }
-    // s: lane l, register jj -> query row 8*(jj/4) + 4*lh + jj%4, key lr.
     const int tok0 = cur.blk * tpb;
-    const bool need_mask = it.causal && (tok0 < wave_kmax);
+    // A causal block whose last row precedes every key of this wave adds
+    // nothing to it.
+    const bool skip = !wave_has_keys || (it.causal && tok0 + tpb - 1 < wave_kmin);
+    if (!skip) {
+      f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int r0 = 8 * g4 + 4 * lh;
-      const f32x4 lv = *reinterpret_cast<const f32x4*>(lse_s + r0);
-      const f32x4 dv = *reinterpret_cast<const f32x4*>(del_s + r0);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int jj = 4 * g4 + e;
-        float p = fast_exp2(s[jj] * c2 - lv[e]);
-        if (need_mask && key_loc > tok0 + (r0 + e) / hp) p = 0.f;
-        s[jj] = p;
-        dp[jj] = p * (dp[jj] - dv[e]);
+      for (int kk = 0; kk < NKK; ++kk) {
+        Frag<T> qa, ga, kb;
+        lds_frag(qa, qs, lr, QROW, 16 * kk + 8 * lh);
+        lds_frag(ga, gs, lr, QROW, 16 * kk + 8 * lh);
+        if constexpr (KLDS) {
+          lds_frag(kb, ktile, krow, QROW, 16 * kk + 8 * lh);
+          mma(s, qa, kb);
+        } else {
+          mma(s, qa, kf[kk]);
+        }
+        mma(dp, ga, vf[kk]);
       }
-    }
-    Frag<T> pf[2], sf[2];
+      // s: lane l, register jj -> query row 8*(jj/4) + 4*lh + jj%4, key lr.
+      const bool need_mask = it.causal && (tok0 < wave_kmax);
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      to_frag(pf[hf], s, 8 * hf);
-      to_frag(sf[hf], dp, 8 * hf);
-    }
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int r0 = 8 * g4 + 4 * lh;
+        const f32x4 lv = *reinterpret_cast<const f32x4*>(lse_s + r0);
+        const f32x4 dv = *reinterpret_cast<const f32x4*>(del_s + r0);
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const int tr = 32 * db + lr;
+        for (int e = 0; e < 4; ++e) {
+          const int jj = 4 * g4 + e;
+          float p = fast_exp2(s[jj] * c2 - lv[e]);
+          if (need_mask && key_loc > tok0 + (r0 + e) / hp) p = 0.f;
+          s[jj] = p;
+          dp[jj] = p * (dp[jj] - dv[e]);
+        }
+      }
+      Frag<T> pf[2], sf[2];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        Frag<T> gt, qt;
-        lds_frag(gt, tgs, tr, QB, 16 * hf + 8 * lh, swz_row<NCHT>(tr));
-        lds_frag(qt, tqs, tr, QB, 16 * hf + 8 * lh, swz_row<NCHT>(tr));
-        mma(dva[db], pf[hf], gt);
-        mma(dka[db], sf[hf], qt);
+        to_frag(pf[hf], s, 8 * hf);
+        to_frag(sf[hf], dp, 8 * hf);
+      }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int tr = 32 * db + lr;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          Frag<T> gt, qt;
+          lds_frag(gt, tgs, tr, TROW, 16 * hf + 8 * lh);
+          lds_frag(qt, tqs, tr, TROW, 16 * hf + 8 * lh);
+          mma(dva[db], pf[hf], gt);
+          mma(dka[db], sf[hf], qt);
+        }
       }
     }
     if (more) lstore(stage ^ 1);
+    wait_vmem();
     __syncthreads();
     cur = nxt;
     stage ^= 1;
@@ -553,7 +501,9 @@ static hipError_t launch_dq_t(const DqLaunch& l, hipStream_t s) {
   a.kt_b_stride = l.kt_b_stride;
   a.scale_log2 = l.scale * kLog2e;
   a.scale = l.scale;
-  const size_t smem = 2 * 3 * (size_t)(32 * KB) * D * sizeof(T);
+  constexpr int CH = 16 / sizeof(T);
+  const size_t smem = 2 * sizeof(T) *
+                      (size_t)(2 * tile_elems<T, 32 * KB, D / CH>() + tile_elems<T, D, 32 * KB / CH>());
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(dq_kernel<T, D, KB>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
@@ -595,7 +545,11 @@ static hipError_t launch_dkv_t(const DkvLaunch& l, hipStream_t s) {
   a.qt_stride = l.qt_stride;
   a.scale_log2 = l.scale * kLog2e;
   a.scale = l.scale;
-  const size_t smem = 2 * 4 * (size_t)32 * D * sizeof(T) + 2 * 2 * 32 * sizeof(float);
+  constexpr int CH = 16 / sizeof(T);
+  const size_t ktile = sizeof(T) == 2 ? (size_t)tile_elems<T, kTileKV, D / CH>() * sizeof(T) : 0;
+  const size_t smem =
+      2 * sizeof(T) * (size_t)(2 * tile_elems<T, 32, D / CH>() + 2 * tile_elems<T, D, 32 / CH>()) +
+      ktile + 2 * 2 * 32 * sizeof(float);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(dkv_kernel<T, D>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
@@ -603,8 +557,8 @@ static hipError_t launch_dkv_t(const DkvLaunch& l, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
   hipEvent_t e0, e1;
   kernel_events(kKernelDkv, &e0, &e1);
-  if (e0) hipExtLaunchKernelGGL(dkv_kernel<T, D>, dim3(grid), dim3(256), smem, s, e0, e1, 0, a);
-  else dkv_kernel<T, D><<<dim3(grid), dim3(256), smem, s>>>(a);
+  if (e0) hipExtLaunchKernelGGL(dkv_kernel<T, D>, dim3(grid), dim3(512), smem, s, e0, e1, 0, a);
+  else dkv_kernel<T, D><<<dim3(grid), dim3(512), smem, s>>>(a);
   return hipGetLastError();
 }
 

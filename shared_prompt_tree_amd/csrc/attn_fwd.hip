@@ -24,6 +24,8 @@
 
 namespace treeattn {
 
+constexpr float kRescale = 8.0f;  // log2 units
+
 template <typename T, int D>
 struct FwdArgs {
   const T* q;
@@ -46,9 +48,10 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdArgs<T, D> a) {
   constexpr int NT = 512, KT = kTileK, CH = ChunkOf<T>::kElems;
   constexpr int NCHK = D / CH;        // 16-byte chunks per K row
   constexpr int NCHV = KT / CH;       // chunks per V^T row
-  constexpr int KTILE = KT * D;       // elements per K (or V^T) tile
-  constexpr int KCH = KT * NCHK, VCH = D * NCHV;
-  constexpr int KPER = (KCH + NT - 1) / NT, VPER = (VCH + NT - 1) / NT;
+  constexpr int KROW = tile_row_elems<T, NCHK>();  // padded row lengths
+  constexpr int VROW = tile_row_elems<T, NCHV>();
+  constexpr int KTILE = tile_elems<T, KT, NCHK>();  // K tile (with slack)
+  constexpr int STAGE = KTILE + tile_elems<T, D, NCHV>();
   constexpr int NKK = D / 16;         // contraction steps over d
   constexpr int NDB = D / 32;         // 32-wide blocks of d
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -83,55 +86,20 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdArgs<T, D> a) {
   const int total = na + nb;
   const size_t kv_stride = (size_t)a.hkv * D;
 
-  u32x4 kst[KPER], vst[VPER];
+  // Tile j into LDS stage j % 2: K rows (keys past the segment are clamped to
+  // its last key and masked later) and V^T rows (padded copy, always in range).
   auto gload = [&](int j) {
     const bool inA = j < na;
     const int ks = (inA ? j : j - na) * KT;
-    const T* kbase = inA ? a.k_a + (size_t)it.a0 * kv_stride : a.k_b + (size_t)it.b0 * kv_stride;
-    const int klen = inA ? it.alen : it.blen;
-#pragma unroll
-    for (int i = 0; i < KPER; ++i) {
-      const int qi = tid + NT * i;
-      if (KCH % NT == 0 || qi < KCH) {
-        const int r = qi / NCHK, c = qi % NCHK;
-        const int key = ks + r;
-        if (key < klen)
-          kst[i] = *reinterpret_cast<const u32x4*>(kbase + (size_t)key * kv_stride + kv * D + c * CH);
-        else
-          kst[i] = u32x4{0, 0, 0, 0};
-      }
-    }
+    const T* kbase = (inA ? a.k_a + (size_t)it.a0 * kv_stride : a.k_b + (size_t)it.b0 * kv_stride) +
+                     (size_t)ks * kv_stride + kv * D;
+    const int klast = (inA ? it.alen : it.blen) - 1 - ks;
+    const int vstride = inA ? a.vt_a_stride : a.vt_b_stride;
     const T* vbase = inA ? a.vt_a + (size_t)kv * D * a.vt_a_stride + it.apad + ks
                          : a.vt_b + (size_t)kv * D * a.vt_b_stride + it.bpad + ks;
-    const int vstride = inA ? a.vt_a_stride : a.vt_b_stride;
-#pragma unroll
-    for (int i = 0; i < VPER; ++i) {
-      const int qi = tid + NT * i;
-      if (VCH % NT == 0 || qi < VCH) {
-        const int dd = qi / NCHV, c = qi % NCHV;
-        vst[i] = *reinterpret_cast<const u32x4*>(vbase + (size_t)dd * vstride + c * CH);
-      }
-    }
-  };
-  auto lstore = [&](int stage) {
-    T* kt = smem + stage * 2 * KTILE;
-    T* vt = kt + KTILE;
-#pragma unroll
-    for (int i = 0; i < KPER; ++i) {
-      const int qi = tid + NT * i;
-      if (KCH % NT == 0 || qi < KCH) {
-        const int r = qi / NCHK, c = qi % NCHK;
-        *reinterpret_cast<u32x4*>(kt + r * D + ((c ^ swz_row<NCHK>(r)) * CH)) = kst[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < VPER; ++i) {
-      const int qi = tid + NT * i;
-      if (VCH % NT == 0 || qi < VCH) {
-        const int dd = qi / NCHV, c = qi % NCHV;
-        *reinterpret_cast<u32x4*>(vt + dd * KT + ((c ^ swz_row<NCHV>(dd)) * CH)) = vst[i];
-      }
-    }
+    T* kt = smem + (j & 1) * STAGE;
+    g2l_tile<T, KT, NCHK, NT>(kt, kbase, [&](int r) { return min(r, klast) * (int)kv_stride; });
+    g2l_tile<T, D, NCHV, NT>(kt + KTILE, vbase, [&](int r) { return r * vstride; });
   };
 
   f32x16 oacc[NDB];
@@ -142,14 +110,12 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdArgs<T, D> a) {
   const float c2 = a.scale_log2;
   const int wave_tok0 = (32 * w) / a.hp;  // smallest token index of this wave
 
-  if (total > 0) {
-    gload(0);
-    lstore(0);
-  }
+  if (total > 0) gload(0);
+  wait_vmem();
   __syncthreads();
   for (int j = 0; j < total; ++j) {
     if (j + 1 < total) gload(j + 1);
-    const T* kt = smem + (j & 1) * 2 * KTILE;
+    const T* kt = smem + (j & 1) * STAGE;
     const T* vt = kt + KTILE;
 
     f32x16 s[2];
@@ -160,7 +126,7 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdArgs<T, D> a) {
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         Frag<T> kf;
-        lds_frag(kf, kt, kr, D, 16 * kk + 8 * lh, swz_row<NCHK>(kr));
+        lds_frag(kf, kt, kr, KROW, 16 * kk + 8 * lh);
         mma(s[kb], kf, qf[kk]);
       }
     }
@@ -185,10 +151,19 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdArgs<T, D> a) {
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj) mx = fmaxf(mx, s[kb][jj]);
     mx = max_with_other_half(mx) * c2;
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    m_run = m_new;
+    // Lazy rescale: the running maximum only has to bound the exponents, so
+    // it is raised (and O and the normaliser rescaled) only when some row of
+    // the wave grew by more than kRescale; otherwise P stays below
+    // 2^kRescale.  The result is the same softmax.
+    if (__any(mx > m_run + kRescale)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
     float ps = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -198,9 +173,7 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdArgs<T, D> a) {
         s[kb][jj] = p;
         ps += p;
       }
-    lsum = lsum * alpha + ps;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+    lsum += ps;
 
     Frag<T> pf[2][2];
 #pragma unroll
@@ -215,12 +188,12 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdArgs<T, D> a) {
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
           Frag<T> vf;
-          lds_frag(vf, vt, vr, KT, 16 * (2 * kb + hf) + 8 * lh, swz_row<NCHV>(vr));
+          lds_frag(vf, vt, vr, VROW, 16 * (2 * kb + hf) + 8 * lh);
           mma(oacc[db], vf, pf[kb][hf]);
         }
     }
 
-    if (j + 1 < total) lstore((j + 1) & 1);
+    wait_vmem();
     __syncthreads();
   }
 
@@ -270,7 +243,9 @@ static hipError_t launch_fwd_t(const FwdLaunch& l, hipStream_t s) {
   a.vt_a_stride = l.vt_a_stride;
   a.vt_b_stride = l.vt_b_stride;
   a.scale_log2 = l.scale * kLog2e;
-  const size_t smem = 2 * 2 * (size_t)kTileK * D * sizeof(T);
+  constexpr int CH = 16 / sizeof(T);
+  const size_t smem =
+      2 * sizeof(T) * (size_t)(tile_elems<T, kTileK, D / CH>() + tile_elems<T, D, kTileK / CH>());
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fwd_kernel<T, D>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;

@@ -64,32 +64,71 @@ __device__ __forceinline__ void load_frag(Frag<float>& f, const float* p) {
   f.v = *reinterpret_cast<const f32x8*>(p);
 }
 
-// Fragment read from an LDS tile stored in 16-byte chunks with an XOR
-// swizzle: element e of row r lives at chunk slot ((e / CH) ^ swz) of that
-// row, where CH is the chunk size in elements.
+// LDS tiles store each row as NCH 16-byte chunks followed by one chunk of
+// padding.  The row stride is then an odd number of chunks, so 16
+// consecutive rows read at the same column fall into 16 different 16-byte
+// bank groups (no bank conflicts), and a fragment address is a per-lane base
+// plus a compile-time offset.
+template <typename T, int NCH>
+__host__ __device__ constexpr int tile_row_elems() {
+  return (NCH + 1) * (16 / (int)sizeof(T));
+}
+
+// Fragment read: 8 elements of row `row` starting at element elem0.
 template <typename T>
 __device__ __forceinline__ void lds_frag(Frag<T>& f, const T* tile, int row, int row_elems,
-                                         int elem0, int swz) {
-  constexpr int CH = ChunkOf<T>::kElems;
-  const T* base = tile + row * row_elems;
-  if constexpr (CH == 8) {
-    f.v = *reinterpret_cast<const bf16x8*>(base + (((elem0 / CH) ^ swz) * CH));
+                                         int elem0) {
+  const T* p = tile + row * row_elems + elem0;
+  if constexpr (sizeof(T) == 2) {
+    f.v = *reinterpret_cast<const bf16x8*>(p);
   } else {
-    f32x4 lo = *reinterpret_cast<const f32x4*>(base + (((elem0 / CH) ^ swz) * CH));
-    f32x4 hi = *reinterpret_cast<const f32x4*>(base + ((((elem0 / CH) + 1) ^ swz) * CH));
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 hi = *reinterpret_cast<const f32x4*>(p + 4);
     f.v = f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
 }
 
-// Chunk-slot XOR for an LDS tile row of NCH 16-byte chunks.  Rows of 256
-// bytes or more are spread by r mod NCH; shorter rows share a 256-byte bank
-// window with their neighbours and are spread by r / (16 / NCH), so any 16
-// consecutive rows read at one chunk index hit 16 different bank groups.
-template <int NCH>
-__device__ __forceinline__ int swz_row(int r) {
-  if constexpr (NCH >= 16) return r & (NCH - 1);
-  else return (r / (16 / NCH)) & (NCH - 1);
+// Elements an LDS tile of ROWS padded rows occupies, rounded up to whole
+// 64-chunk wave copies (the slack receives harmless duplicate chunks).
+template <typename T, int ROWS, int NCH>
+__host__ __device__ constexpr int tile_elems() {
+  return ((ROWS * (NCH + 1) + 63) / 64) * 64 * (16 / (int)sizeof(T));
 }
+
+// Copy a tile of ROWS rows x NCH 16-byte chunks from global memory straight
+// into its padded LDS layout (global_load_lds_dwordx4: no registers
+// involved).  One wave instruction fills 64 consecutive LDS chunks, lane l
+// writing chunk l of them.  Lanes that land on a padding chunk or in the
+// slack load a duplicate of a real chunk, so no lane is switched off.
+// Global addresses are the wave-uniform `base` plus row_off(r) + chunk
+// offset in elements (32-bit; the caller clamps rows past the end to a
+// valid row).  Completion is awaited with wait_vmem() before the barrier
+// that publishes the tile.
+template <typename T, int ROWS, int NCH, int NT, typename RowOff>
+__device__ __forceinline__ void g2l_tile(T* tile, const T* base, RowOff row_off) {
+  constexpr int CH = 16 / sizeof(T);
+  constexpr int STRIDE = NCH + 1;
+  constexpr int NCHUNK = tile_elems<T, ROWS, NCH>() / CH;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < (NCHUNK + NT - 1) / NT; ++i) {
+    const int p0 = i * NT + 64 * w;  // first chunk of this wave instruction
+    if (NCHUNK % NT == 0 || p0 < NCHUNK) {
+      const int p = p0 + lane;
+      const int q = p / STRIDE;
+      const int r = q < ROWS ? q : ROWS - 1;
+      const int s = min(p - q * STRIDE, NCH - 1);
+      const uint32_t off = (uint32_t)row_off(r) + (uint32_t)(s * CH);
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(base + off),
+          (__attribute__((address_space(3))) void*)(tile + p0 * CH), 16, 0, 0);
+    }
+  }
+}
+
+// Wait until this wave's outstanding memory operations (including the
+// global-to-LDS copies above) have completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
 
 // Convert 8 float32 (registers j0..j0+7 of an output block) to an operand
 // fragment.  bf16 rounds to nearest even.
@@ -181,7 +220,7 @@ struct KItem {
 
 constexpr int kTileQ = 256;  // query rows per workgroup (query-stationary)
 constexpr int kTileK = 64;   // keys per step (query-stationary)
-constexpr int kTileKV = 128; // keys per workgroup (key-stationary)
+constexpr int kTileKV = 256; // keys per workgroup (key-stationary)
 constexpr int kBlockQ = 64;  // query rows per step (key-stationary)
 constexpr int kPad = 64;     // token padding of every segment in transposed copies
 
