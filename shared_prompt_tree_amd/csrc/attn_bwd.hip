@@ -293,27 +293,30 @@ __global__ __launch_bounds__(512) void dkv_kernel(DkvArgs<T, D> a) {
     g2l_tile<T, 32 * NW, NCHQ, NT>(ktile, kb, [&](int r) { return min(r, it.nk - 1) * (int)kv_stride; });
   }
 
-  // Query block cursor: head sub-group hs, segment seg, block blk.
+  // Query block cursor: head sub-group hs, segment seg, block blk.  Blocks
+  // are visited from the last one backwards, so the key tiles of a segment
+  // that run at the same time (they start together, see the work-list
+  // order) read the same query blocks at the same time and share them in
+  // L2.  A causal tile stops at the block holding its first key.
   struct Cur {
-    int hs, seg, blk, nblk, q0, nq, qpad;
+    int hs, seg, blk, blk_lo, q0, nq, qpad;
   };
-  const int blk0 = it.causal ? (it.kpos / tpb) : 0;
   auto seg_init = [&](Cur& c) {
     c.q0 = a.seg_cu[c.seg];
     c.nq = a.seg_cu[c.seg + 1] - c.q0;
     c.qpad = a.seg_pad[c.seg];
-    c.nblk = (c.nq + tpb - 1) / tpb;
-    c.blk = blk0;
+    c.blk = (c.nq + tpb - 1) / tpb - 1;
+    c.blk_lo = it.causal ? (it.kpos / tpb) : 0;
   };
   auto settle = [&](Cur& c) -> bool {  // move to the next non-empty block
     while (true) {
-      if (c.hs >= a.nsub) return false;
-      if (c.seg < it.seg_hi && c.blk < c.nblk) return true;
-      if (c.seg < it.seg_hi) ++c.seg;
-      if (c.seg >= it.seg_hi) {
-        c.seg = it.seg_lo;
-        ++c.hs;
-        if (c.hs >= a.nsub || it.seg_lo >= it.seg_hi) return false;
+      if (c.hs < 0) return false;
+      if (c.seg >= it.seg_lo && c.blk >= c.blk_lo) return true;
+      if (c.seg >= it.seg_lo) --c.seg;
+      if (c.seg < it.seg_lo) {
+        c.seg = it.seg_hi - 1;
+        --c.hs;
+        if (c.hs < 0 || it.seg_lo >= it.seg_hi) return false;
       }
       seg_init(c);
     }
@@ -362,7 +365,7 @@ __global__ __launch_bounds__(512) void dkv_kernel(DkvArgs<T, D> a) {
   const bool wave_has_keys = 32 * w < it.nk;
   const int krow = 32 * w + lr;               // this lane's row of the K tile
 
-  Cur cur{0, it.seg_lo, 0, 0, 0, 0, 0};
+  Cur cur{a.nsub - 1, it.seg_hi - 1, 0, 0, 0, 0, 0};
   bool have = false;
   if (it.seg_lo < it.seg_hi) {
     seg_init(cur);
@@ -377,7 +380,7 @@ __global__ __launch_bounds__(512) void dkv_kernel(DkvArgs<T, D> a) {
   int stage = 0;
   while (have) {
     Cur nxt = cur;
-    ++nxt.blk;
+    --nxt.blk;
     const bool more = settle(nxt);
     if (more) gload(nxt, stage ^ 1);
     const T* qs = smem + stage * STAGE;

@@ -7,16 +7,15 @@ namespace treeattn {
 
 // ------------------------------------------------------------ work lists
 //
-// One workgroup derives every tile of the launch from the device offset
-// arrays and writes them in decreasing cost (longest-processing-time first:
-// the heaviest tiles start first, which evens out the tail).  The same idea
-// orders replay units largest first in the AugTree planner (section 3.4).
-// Costs are counted in 64-key steps (query-stationary tiles) or 32-row
-// blocks (key-stationary tiles); a counting sort over at most kBuckets
-// levels keeps the order approximate for very long tiles.
+// One workgroup derives every tile of a launch from the device offset arrays.
+// Tiles are ordered segment by segment, longest segment first (in the
+// spirit of the largest-first unit assignment of the AugTree planner,
+// section 3.4), and within a segment longest tile first.  Workgroups are
+// dealt to the XCDs in this order, so the tiles of one segment run at the
+// same time on the same XCD and share its keys / queries in that XCD's L2.
 
 constexpr int kMetaThreads = 1024;
-constexpr int kBuckets = 2048;
+constexpr int kRankMax = 4096;  // segments ranked by length up to this count
 
 __device__ int block_exclusive_scan(int v, int* sh) {
   // sh: kMetaThreads ints.  Returns the exclusive prefix; sh[last] holds the
@@ -56,9 +55,6 @@ __device__ __forceinline__ int pad_len(int n) { return ceil_div(n, kPad) * kPad;
 
 __global__ __launch_bounds__(kMetaThreads) void meta_kernel(MetaArgs a) {
   __shared__ int sh[kMetaThreads];
-  __shared__ int hist[kBuckets];
-  __shared__ int cursor[kBuckets];
-  __shared__ int max_cost;
   const int t = threadIdx.x;
   const int ng = a.n_groups, nbr = a.n_branches;
   const int32_t* pcu = a.prompt_cu;
@@ -74,52 +70,68 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(MetaArgs a) {
   }
   __syncthreads();
 
-  // sources and their tile counts
+  // Sources (segments that own tiles), their tile counts and ranking keys.
+  // Replay key-stationary launches hold the prompt tiles of every group
+  // (they read all response rows of the group; ranked first) followed by
+  // the own-branch tiles.
   const int tq = a.tile_q;
-  int nsrc = 0;
+  int nsrc;
   if (a.mode == kMetaQPrefill || a.mode == kMetaKPrefill) nsrc = ng;
   else if (a.mode == kMetaQReplay) nsrc = nbr;
   else nsrc = ng + nbr;
-  auto tiles_of = [&](int s) -> int {
+  auto seg_len = [&](int s) -> int {
     switch (a.mode) {
-      case kMetaQPrefill: return ceil_div(pcu[s + 1] - pcu[s], tq);
-      case kMetaQReplay: return ceil_div(rcu[s + 1] - rcu[s], tq);
-      case kMetaKPrefill: return ceil_div(pcu[s + 1] - pcu[s], kTileKV);
-      default:
-        return s < ng ? ceil_div(pcu[s + 1] - pcu[s], kTileKV)
-                      : ceil_div(rcu[s - ng + 1] - rcu[s - ng], kTileKV);
+      case kMetaQPrefill:
+      case kMetaKPrefill: return pcu[s + 1] - pcu[s];
+      case kMetaQReplay: return rcu[s + 1] - rcu[s];
+      default: return s < ng ? pcu[s + 1] - pcu[s] : rcu[s - ng + 1] - rcu[s - ng];
     }
   };
-  int n = scan_into(nsrc, tiles_of, a.src_cu, sh);
+  auto tiles_of = [&](int s) -> int {
+    const int len = seg_len(s);
+    return (a.mode == kMetaQPrefill || a.mode == kMetaQReplay) ? ceil_div(len, tq)
+                                                              : ceil_div(len, kTileKV);
+  };
+  auto key_of = [&](int s) -> int {
+    if (a.mode == kMetaKReplay && s < ng) return (1 << 30) + (ng - s);
+    return seg_len(s);
+  };
+  // rank by decreasing key, ties by index; order[rank] = source
+  for (int s = t; s < nsrc; s += kMetaThreads) {
+    int rank = s;
+    if (nsrc <= kRankMax) {
+      const int ks = key_of(s);
+      rank = 0;
+      for (int u = 0; u < nsrc; ++u) {
+        const int ku = key_of(u);
+        rank += (ku > ks) || (ku == ks && u < s);
+      }
+    }
+    a.src_order[rank] = s;
+  }
+  __syncthreads();
+  int n = scan_into(nsrc, [&](int k) { return tiles_of(a.src_order[k]); }, a.src_cu, sh);
   if (n > a.cap) n = a.cap;
   const bool qmode = a.mode == kMetaQPrefill || a.mode == kMetaQReplay;
-  QItem* qtmp = static_cast<QItem*>(a.items_tmp);
-  KItem* ktmp = static_cast<KItem*>(a.items_tmp);
   QItem* qout = static_cast<QItem*>(a.items);
   KItem* kout = static_cast<KItem*>(a.items);
-
-  if (t == 0) max_cost = 0;
-  for (int b = t; b < kBuckets; b += kMetaThreads) {
-    hist[b] = 0;
-    cursor[b] = 0;
-  }
-  // empty items everywhere first, so a short list never leaves stale slots
-  for (int i = t; i < a.cap; i += kMetaThreads) {
+  for (int i = n + t; i < a.cap; i += kMetaThreads) {  // never leave a stale slot
     if (qmode) qout[i] = QItem{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
     else kout[i] = KItem{0, 0, 0, 0, 0, 0, 0, 0};
   }
-  __syncthreads();
 
   for (int i = t; i < n; i += kMetaThreads) {
-    int lo = 0, hi = nsrc - 1;  // last source with src_cu[s] <= i
+    int lo = 0, hi = nsrc - 1;  // last rank with src_cu[k] <= i
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (a.src_cu[mid] <= i) lo = mid;
       else hi = mid - 1;
     }
-    const int s = lo, tile = i - a.src_cu[s];
-    int cost;
+    const int s = a.src_order[lo];
+    const int u = i - a.src_cu[lo];
     if (qmode) {
+      // query tiles: the last tile of a causal segment reads the most keys
+      const int tile = tiles_of(s) - 1 - u;
       QItem q;
       q.r0 = q.r1 = 0;
       if (a.mode == kMetaQPrefill) {
@@ -146,10 +158,11 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(MetaArgs a) {
         q.blen = q.qpos + q.nq;
         q.bpad = a.resp_pad[s];
       }
-      cost = ceil_div(q.alen, kTileK) + ceil_div(q.blen, kTileK);
-      q.cost = cost;
-      qtmp[i] = q;
+      q.cost = ceil_div(q.alen, kTileK) + ceil_div(q.blen, kTileK);
+      qout[i] = q;
     } else {
+      // key tiles: the first tile of a causal segment is read by the most rows
+      const int tile = u;
       KItem k;
       if (a.mode == kMetaKPrefill) {
         const int plen = pcu[s + 1] - pcu[s];
@@ -160,7 +173,7 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(MetaArgs a) {
         k.seg_lo = s;
         k.seg_hi = s + 1;
         k.causal = 1;
-        cost = plen - k.kpos;
+        k.cost = plen - k.kpos;
       } else if (s < ng) {  // prompt tile in replay: every branch of the group
         const int plen = pcu[s + 1] - pcu[s];
         k.kpos = tile * kTileKV;
@@ -170,7 +183,7 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(MetaArgs a) {
         k.seg_lo = gcu[s];
         k.seg_hi = gcu[s + 1];
         k.causal = 0;
-        cost = rcu[gcu[s + 1]] - rcu[gcu[s]];
+        k.cost = rcu[gcu[s + 1]] - rcu[gcu[s]];
       } else {  // own-branch tile
         const int b = s - ng;
         const int rlen = rcu[b + 1] - rcu[b];
@@ -181,43 +194,9 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(MetaArgs a) {
         k.seg_lo = b;
         k.seg_hi = b + 1;
         k.causal = 1;
-        cost = rlen - k.kpos;
+        k.cost = rlen - k.kpos;
       }
-      cost = ceil_div(cost, 32);
-      k.cost = cost;
-      ktmp[i] = k;
-    }
-    atomicMax(&max_cost, cost);
-  }
-  __syncthreads();
-  const int mc = max_cost;
-  auto bucket_of = [&](int c) -> int {
-    // larger cost -> smaller bucket index (sorted first)
-    const long long b = (long long)(mc - c) * (kBuckets - 1) / (mc > 0 ? mc : 1);
-    return (int)(b < 0 ? 0 : (b > kBuckets - 1 ? kBuckets - 1 : b));
-  };
-  for (int i = t; i < n; i += kMetaThreads)
-    atomicAdd(&hist[bucket_of(qmode ? qtmp[i].cost : ktmp[i].cost)], 1);
-  __syncthreads();
-  // exclusive scan of hist (kBuckets = 2 * kMetaThreads entries)
-  {
-    const int b0 = 2 * t, b1 = 2 * t + 1;
-    const int v = hist[b0] + hist[b1];
-    const int ex = block_exclusive_scan(v, sh);
-    __syncthreads();
-    const int h0 = hist[b0];
-    __syncthreads();
-    hist[b0] = ex;
-    hist[b1] = ex + h0;
-  }
-  __syncthreads();
-  for (int i = t; i < n; i += kMetaThreads) {
-    const int c = qmode ? qtmp[i].cost : ktmp[i].cost;
-    const int b = bucket_of(c);
-    const int pos = hist[b] + atomicAdd(&cursor[b], 1);
-    if (pos < a.cap) {
-      if (qmode) qout[pos] = qtmp[i];
-      else kout[pos] = ktmp[i];
+      kout[i] = k;
     }
   }
 }

@@ -27,9 +27,9 @@ struct MetaArgs {
   int32_t* prompt_pad;    // [n_groups + 1] out: padded token offsets
   int32_t* resp_pad;      // [n_branches + 1] out
   int32_t* branch_group;  // [n_branches] out
-  int32_t* src_cu;        // [n_sources + 1] scratch
-  void* items_tmp;        // [cap] scratch
-  void* items;            // [cap] out, sorted by decreasing cost
+  int32_t* src_cu;        // [n_sources + 1] scratch: tile offsets in rank order
+  int32_t* src_order;     // [n_sources + 1] scratch: source of each rank
+  void* items;            // [cap] out, segment-major
   int cap;                // number of items the host computed
   int tile_q;             // query tokens per query-stationary tile
 };

@@ -115,7 +115,7 @@ struct MetaBufs {
   int32_t* resp_pad;
   int32_t* branch_group;
   int32_t* src_cu;
-  void* tmp;
+  int32_t* src_order;
   void* items;
 };
 
@@ -125,7 +125,7 @@ MetaBufs take_meta(Carve& c, const Shape& s, long long cap, size_t item_bytes) {
   m.resp_pad = static_cast<int32_t*>(c.take((s.nb + 1) * sizeof(int32_t)));
   m.branch_group = static_cast<int32_t*>(c.take((s.nb + 1) * sizeof(int32_t)));
   m.src_cu = static_cast<int32_t*>(c.take((s.ng + s.nb + 1) * sizeof(int32_t)));
-  m.tmp = c.take(std::max<long long>(cap, 1) * item_bytes);
+  m.src_order = static_cast<int32_t*>(c.take((s.ng + s.nb + 1) * sizeof(int32_t)));
   m.items = c.take(std::max<long long>(cap, 1) * item_bytes);
   return m;
 }
@@ -228,7 +228,7 @@ hipError_t run_meta(const tree_attn_problem* p, const Shape& s, const MetaBufs& 
   a.resp_pad = m.resp_pad;
   a.branch_group = m.branch_group;
   a.src_cu = m.src_cu;
-  a.items_tmp = m.tmp;
+  a.src_order = m.src_order;
   a.items = m.items;
   a.cap = (int)cap;
   a.tile_q = s.tile_q;
