@@ -301,10 +301,12 @@ __global__ __launch_bounds__(512) void dkv_kernel(DkvArgs<T, D> a) {
   struct Cur {
     int hs, seg, blk, blk_lo, q0, nq, qpad;
   };
+  // The offsets are read into scalar registers at once, so waiting for
+  // them never waits for global-to-LDS copies issued later.
   auto seg_init = [&](Cur& c) {
-    c.q0 = a.seg_cu[c.seg];
-    c.nq = a.seg_cu[c.seg + 1] - c.q0;
-    c.qpad = a.seg_pad[c.seg];
+    c.q0 = __builtin_amdgcn_readfirstlane(a.seg_cu[c.seg]);
+    c.nq = __builtin_amdgcn_readfirstlane(a.seg_cu[c.seg + 1]) - c.q0;
+    c.qpad = __builtin_amdgcn_readfirstlane(a.seg_pad[c.seg]);
     c.blk = (c.nq + tpb - 1) / tpb - 1;
     c.blk_lo = it.causal ? (it.kpos / tpb) : 0;
   };
@@ -326,6 +328,7 @@ __global__ __launch_bounds__(512) void dkv_kernel(DkvArgs<T, D> a) {
   // clamped to its last token; their LSE is +inf so they add nothing), Q^T
   // and dO^T rows (padded copies), and LSE*log2(e) and D through registers.
   float lst = 0.f;
+  bool lvalid = false;
   auto gload = [&](const Cur& c, int stage) {
     const int hg = kv * a.nsub + c.hs;
     const int tok0 = c.blk * tpb;
@@ -340,16 +343,23 @@ __global__ __launch_bounds__(512) void dkv_kernel(DkvArgs<T, D> a) {
     auto trow = [&](int r) { return r * a.qt_stride; };
     g2l_tile<T, D, NCHT, NT>(qs + 2 * QTILE, a.qt + tb, trow);
     g2l_tile<T, D, NCHT, NT>(qs + 2 * QTILE + TTILE, a.dot + tb, trow);
+    // The raw value is only used in lstore at the end of the block, so the
+    // wait for this load does not hold up the block's LDS reads.
     if (tid < 2 * QB) {
       const int r = tid & (QB - 1);
       const int tok = tok0 + r / hp;
-      const size_t li = (size_t)(hg * hp + (r % hp)) * a.lse_stride + c.q0 + tok;
-      if (tid < QB) lst = tok < c.nq ? a.lse[li] * kLog2e : INFINITY;
-      else lst = tok < c.nq ? a.delta[li] : 0.f;
+      lvalid = tok < c.nq;
+      const size_t li =
+          (size_t)(hg * hp + (r % hp)) * a.lse_stride + c.q0 + (lvalid ? tok : c.nq - 1);
+      lst = tid < QB ? a.lse[li] : a.delta[li];
     }
   };
+  // LSE is kept as LSE * log2(e); rows past the segment get LSE = +inf
+  // (P = 0) and D = 0.
   auto lstore = [&](int stage) {
-    if (tid < 2 * QB) fsm[stage * 2 * QB + tid] = lst;
+    if (tid < 2 * QB)
+      fsm[stage * 2 * QB + tid] =
+          tid < QB ? (lvalid ? lst * kLog2e : INFINITY) : (lvalid ? lst : 0.f);
   };
 
   f32x16 dka[NDB], dva[NDB];
@@ -409,7 +419,10 @@ __global__ __launch_bounds__(512) void dkv_kernel(DkvArgs<T, D> a) {
         mma(dp, ga, vf[kk]);
       }
       // s: lane l, register jj -> query row 8*(jj/4) + 4*lh + jj%4, key lr.
+      // Causal mask: row r (token tok0 + r/hp) is hidden from this lane's
+      // key iff r < (key - tok0) * hp, i.e. 8*(jj/4) + jj%4 < row_lim.
       const bool need_mask = it.causal && (tok0 < wave_kmax);
+      const int row_lim = (key_loc - tok0) * hp - 4 * lh;
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int r0 = 8 * g4 + 4 * lh;
@@ -419,7 +432,7 @@ __global__ __launch_bounds__(512) void dkv_kernel(DkvArgs<T, D> a) {
         for (int e = 0; e < 4; ++e) {
           const int jj = 4 * g4 + e;
           float p = fast_exp2(s[jj] * c2 - lv[e]);
-          if (need_mask && key_loc > tok0 + (r0 + e) / hp) p = 0.f;
+          if (need_mask && 8 * g4 + e < row_lim) p = 0.f;
           s[jj] = p;
           dp[jj] = p * (dp[jj] - dv[e]);
         }

@@ -88,6 +88,23 @@ __device__ __forceinline__ void lds_frag(Frag<T>& f, const T* tile, int row, int
   }
 }
 
+// One global_load_lds_dwordx4: every lane copies 16 bytes from its own
+// global address to LDS byte (lds_wave_dst + 16 * lane), lds_wave_dst being
+// uniform across the wave (it goes through M0).  The instruction is issued
+// from inline assembly so the compiler does not treat it as a pending LDS
+// write and stall later LDS reads of other buffers on it; the caller waits
+// for completion (wait_vmem) before the barrier that publishes the data.
+// Memory reads return in issue order, so any wait the compiler places for
+// its own loads stays correct.
+__device__ __forceinline__ void dma_16(const void* src, void* lds_wave_dst) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_wave_dst);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds)
+               : "m0");
+}
+
 // Elements an LDS tile of ROWS padded rows occupies, rounded up to whole
 // 64-chunk wave copies (the slack receives harmless duplicate chunks).
 template <typename T, int ROWS, int NCH>
@@ -119,9 +136,7 @@ __device__ __forceinline__ void g2l_tile(T* tile, const T* base, RowOff row_off)
       const int r = q < ROWS ? q : ROWS - 1;
       const int s = min(p - q * STRIDE, NCH - 1);
       const uint32_t off = (uint32_t)row_off(r) + (uint32_t)(s * CH);
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(base + off),
-          (__attribute__((address_space(3))) void*)(tile + p0 * CH), 16, 0, 0);
+      dma_16(base + off, tile + p0 * CH);
     }
   }
 }
