@@ -39,6 +39,43 @@ HBM_GBPS = 8000.0
 KERNEL_FLOPS_PER_PAIR_DIM = {"fwd": 4, "dq": 6, "dkv": 8}
 
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "roofline_traffic.json")
+# Sources each main kernel is built from; a stored traffic figure is only
+# reported while these are unchanged.
+KERNEL_SOURCES = {
+    "fwd": ["attn_fwd.hip", "device_common.h"],
+    "dq": ["attn_bwd.hip", "device_common.h"],
+    "dkv": ["attn_bwd.hip", "device_common.h"],
+}
+KERNEL_SYMBOLS = {"fwd": "fwd_kernel", "dq": "dq_kernel", "dkv": "dkv_kernel"}
+
+
+def kernel_source_hash(kind):
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, "shared_prompt_tree_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kind):
+    """HBM bytes per launch measured by rocprofv3 for this kernel, if the
+    measurement was taken on the current sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    k = rec.get("kernels", {}).get(kind)
+    if not k or k.get("source_hash") != kernel_source_hash(kind):
+        return None
+    return k.get("hbm_bytes_per_launch")
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -50,6 +87,11 @@ def parse():
     p.add_argument("--no-flattened", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-workers", type=int, default=0)
+    p.add_argument("--summarize", nargs="+", metavar="DIR",
+                   help="write profiles/ summaries from rocprofv3 output directories "
+                        "(kernel-trace stats, FETCH_SIZE and WRITE_SIZE passes) and exit")
+    p.add_argument("--summarize-command", default="",
+                   help="the profiling command recorded in the summaries")
     p.add_argument("--copy-calibration-mib", type=int, default=1024,
                    help="size of a plain device copy run after the timed region, used to "
                         "scale HBM byte counters in profiling runs (0 to skip)")
@@ -135,7 +177,6 @@ def measure_workload(name, steps, warmup, flattened=True):
             part[n] += evs[i].elapsed_time(evs[i + 1]) / steps
         for (k, c), (a, b) in kev.items():
             kern[k] += a.elapsed_time(b) / steps
-    per_call = {}  # the biggest single launch of each kernel kind
 
     pairs = wl.pair_counts(tree)
     useful = wl.useful_flops(tree)
@@ -155,12 +196,11 @@ def measure_workload(name, steps, warmup, flattened=True):
     rep["roofline"] = {
         "kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
         "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
-        "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+        "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": stored_traffic(dom),
         "flops_per_pair_per_dim": KERNEL_FLOPS_PER_PAIR_DIM[dom],
         "launches_per_step": 2, "ms_per_step": round(kern[dom], 4),
     }
     rep["kernel_tflops"] = {k: round(kflops[k] / (kern[k] * 1e-3) / 1e12, 2) for k in kern}
-    del per_call
 
     if flattened:
         ftree = wl.flattened_tree(tree)
@@ -260,8 +300,85 @@ def _cpu_unit(k):
     return k
 
 
+def _csv_rows(dirs, suffix):
+    import csv
+    import glob
+
+    out = []
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True):
+            with open(f) as fh:
+                out.extend(csv.DictReader(fh))
+    return out
+
+
+def summarize(dirs, command):
+    """profiles/ summaries from rocprofv3 CSV output (kernel_stats,
+    kernel_trace and counter_collection files)."""
+    os.makedirs(PROFILES, exist_ok=True)
+    lines = []
+    stats = _csv_rows(dirs, "_kernel_stats.csv")
+    if stats:
+        lines.append("kernel                      calls   avg ms    total ms   share")
+        for r in stats:
+            name = r["Name"]
+            short = next((k for k, v in KERNEL_SYMBOLS.items() if v in name), None)
+            label = short or name.split("(")[0][:26]
+            lines.append(f"{label:26s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e6:8.3f} "
+                         f"{float(r['TotalDurationNs']) / 1e6:10.3f}  {float(r['Percentage']):5.1f}%")
+    counters = {}
+    for r in _csv_rows(dirs, "_counter_collection.csv"):
+        counters.setdefault(r["Counter_Name"], []).append(r)
+    traffic = {}
+    calib = {}
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        rows = counters.get(ctr, [])
+        copy = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        big = max(copy) if copy else 0.0
+        # the calibration copy moves 1 GiB = 1048576 KiB each way
+        calib[ctr] = 1048576.0 / big if big > 0 else None
+        for kind, sym in KERNEL_SYMBOLS.items():
+            vals = [float(r["Counter_Value"]) for r in rows if sym in r["Kernel_Name"]]
+            if vals and calib[ctr]:
+                traffic.setdefault(kind, {})[ctr] = [v * 1024 * calib[ctr] for v in vals]
+    if traffic:
+        lines.append("")
+        lines.append("HBM bytes per launch (KiB counter x 1024 x calibration), launches in order:")
+        lines.append(f"calibration from a 1 GiB device copy: FETCH_SIZE x{calib['FETCH_SIZE']:.3f}, "
+                     f"WRITE_SIZE x{calib['WRITE_SIZE']:.3f}")
+        rec = {"kernels": {}, "calibration": calib, "command": command}
+        for kind, d in traffic.items():
+            f = d.get("FETCH_SIZE", [])
+            w = d.get("WRITE_SIZE", [])
+            lines.append(f"{kind:4s} read  GB: " + " ".join(f"{x / 1e9:.3f}" for x in f))
+            lines.append(f"{kind:4s} write GB: " + " ".join(f"{x / 1e9:.3f}" for x in w))
+            if f and w:
+                per = (sum(f) + sum(w)) / max(len(f), len(w))
+                rec["kernels"][kind] = {"hbm_bytes_per_launch": round(per),
+                                        "source_hash": kernel_source_hash(kind),
+                                        "read_bytes": [round(x) for x in f],
+                                        "write_bytes": [round(x) for x in w]}
+        with open(TRAFFIC_FILE, "w") as fh:
+            json.dump(rec, fh, indent=1)
+    other = {c: v for c, v in counters.items() if c not in ("FETCH_SIZE", "WRITE_SIZE")}
+    if other:
+        lines.append("")
+        lines.append("counter totals per kernel (summed over dispatches):")
+        for kind, sym in KERNEL_SYMBOLS.items():
+            row = []
+            for c in sorted(other):
+                v = sum(float(r["Counter_Value"]) for r in other[c] if sym in r["Kernel_Name"])
+                row.append(f"{c}={v:.4g}")
+            lines.append(f"{kind}: " + " ".join(row))
+    head = ["rocprofv3 summary", f"command: {command}", ""]
+    return "\n".join(head + lines) + "\n"
+
+
 def main():
     args = parse()
+    if args.summarize:
+        print(summarize(args.summarize, args.summarize_command), end="")
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         fail("bench.py measures one GPU: this build has no multi-GPU path "
              "(every box has one GPU); run with --gpus 1")
