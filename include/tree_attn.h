@@ -36,6 +36,12 @@
  * Streams.  Each call only enqueues work on `stream` (a hipStream_t; NULL is
  * the default stream) and never synchronises.  Calls that share workspace
  * must be ordered on one stream.
+ * Sizes.  Token totals times Hq, and padded token totals (each prompt and
+ * branch rounded up to 64) times the packed head count, must fit in int32;
+ * head_dim * padded tokens * packed heads * element size must stay below
+ * 4 GiB.  The packed head count is the largest power of two (at most 16)
+ * dividing Hq / Hkv.  Larger problems are rejected with
+ * TREE_ATTN_ERR_INVALID.
  * Errors.  0 on success, else a negative tree_attn_status.  Arguments are
  * checked on the host before any HIP call, so a rejected call enqueues
  * nothing and writes nothing.  TREE_ATTN_ERR_HIP reports a failed launch.

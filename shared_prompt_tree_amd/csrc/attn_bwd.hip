@@ -9,7 +9,10 @@
 // query row that reads them, for all query heads of that kv head.  For a
 // prompt tile in replay that is every response row of every branch of the
 // group, so the sum over branches of Eq. 2 happens in the accumulators and
-// the float32 seeds are written once, without atomics.  Query rows stream
+// the float32 seeds are written once, without atomics.  (Where one group's
+// response rows are far more than a fair share of the launch, its branches
+// are cut into a few ranges, each writing a partial sum that a small kernel
+// adds in a fixed order.)  Query rows stream
 // through LDS in blocks of 32, double buffered; Q^T and dO^T come from
 // pre-transposed copies so that every operand is read with 16-byte LDS
 // loads.
@@ -19,6 +22,7 @@
 // segment B (causal).  It recomputes P and dP per tile and accumulates
 // dQ^T += K^T dS^T with K^T read from a pre-transposed copy.
 #include <hip/hip_ext.h>
+#include <type_traits>
 
 #include "device_common.h"
 #include "launch.h"
@@ -226,6 +230,8 @@ struct DkvArgs {
   T* dv;
   float* dk_seed;
   float* dv_seed;
+  float* part_k;
+  float* part_v;
   const KItem* items;
   int n_items;
   int hq, hkv, hp, nsub;
@@ -260,7 +266,7 @@ __global__ __launch_bounds__(512) void dkv_kernel(DkvArgs<T, D> a) {
   if (!xcd_map(blockIdx.x, a.n_items, a.hkv, item_idx, kv)) return;
   const KItem it = a.items[item_idx];
   if (it.nk <= 0) return;
-  if (it.kind == 1 && a.dk_seed == nullptr) return;  // detached prompt: no seeds wanted
+  if ((it.kind == 1 || it.kind == 3) && a.dk_seed == nullptr) return;  // detached prompt
   const T* ksrc = it.kind == 0 ? a.k : a.k_prompt;
   const T* vsrc = it.kind == 0 ? a.v : a.v_prompt;
 
@@ -423,20 +429,26 @@ __global__ __launch_bounds__(512) void dkv_kernel(DkvArgs<T, D> a) {
       // key iff r < (key - tok0) * hp, i.e. 8*(jj/4) + jj%4 < row_lim.
       const bool need_mask = it.causal && (tok0 < wave_kmax);
       const int row_lim = (key_loc - tok0) * hp - 4 * lh;
+      auto grad_scores = [&](auto masked) {
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int r0 = 8 * g4 + 4 * lh;
-        const f32x4 lv = *reinterpret_cast<const f32x4*>(lse_s + r0);
-        const f32x4 dv = *reinterpret_cast<const f32x4*>(del_s + r0);
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int r0 = 8 * g4 + 4 * lh;
+          const f32x4 lv = *reinterpret_cast<const f32x4*>(lse_s + r0);
+          const f32x4 dv = *reinterpret_cast<const f32x4*>(del_s + r0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int jj = 4 * g4 + e;
-          float p = fast_exp2(s[jj] * c2 - lv[e]);
-          if (need_mask && 8 * g4 + e < row_lim) p = 0.f;
-          s[jj] = p;
-          dp[jj] = p * (dp[jj] - dv[e]);
+          for (int e = 0; e < 4; ++e) {
+            const int jj = 4 * g4 + e;
+            float p = fast_exp2(s[jj] * c2 - lv[e]);
+            if constexpr (decltype(masked)::value) {
+              if (8 * g4 + e < row_lim) p = 0.f;
+            }
+            s[jj] = p;
+            dp[jj] = p * (dp[jj] - dv[e]);
+          }
         }
-      }
+      };
+      if (need_mask) grad_scores(std::true_type{});
+      else grad_scores(std::false_type{});
       Frag<T> pf[2], sf[2];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
@@ -471,6 +483,7 @@ __global__ __launch_bounds__(512) void dkv_kernel(DkvArgs<T, D> a) {
     const int key = 32 * w + 8 * (jj >> 2) + 4 * lh + (jj & 3);
     if (key >= it.nk) continue;
     const size_t base = (size_t)(it.k0 + key) * kv_stride + kv * D;
+    const size_t pbase = (size_t)(it.prow + key) * kv_stride + kv * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       const size_t o = base + 32 * db + lr;
@@ -479,6 +492,9 @@ __global__ __launch_bounds__(512) void dkv_kernel(DkvArgs<T, D> a) {
       if (it.kind == 1) {
         a.dk_seed[o] = gk;
         a.dv_seed[o] = gv;
+      } else if (it.kind == 3) {
+        a.part_k[pbase + 32 * db + lr] = gk;
+        a.part_v[pbase + 32 * db + lr] = gv;
       } else {
         if (it.kind == 2 && a.dk_seed != nullptr) {
           gk += a.dk_seed[o];
@@ -551,6 +567,8 @@ static hipError_t launch_dkv_t(const DkvLaunch& l, hipStream_t s) {
   a.dv = static_cast<T*>(l.dv);
   a.dk_seed = l.dk_seed;
   a.dv_seed = l.dv_seed;
+  a.part_k = l.part_k;
+  a.part_v = l.part_v;
   a.items = static_cast<const KItem*>(l.items);
   a.n_items = l.n_items;
   a.hq = l.hq;

@@ -70,10 +70,47 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(MetaArgs a) {
   }
   __syncthreads();
 
+  // Replay key-stationary lists: the prompt tiles of a group read every
+  // response row of the group.  Where that is far more than a fair share of
+  // the launch, the group's branches are cut into splits (contiguous branch
+  // ranges with balanced row counts, at least one branch each); each split
+  // of each prompt tile is its own work item writing float32 partial seeds,
+  // summed afterwards in a fixed order.
+  const bool ksplit = a.mode == kMetaKReplay;
+  auto splits_of = [&](int g) {
+    return prompt_splits(gcu[g + 1] - gcu[g], (long long)rcu[gcu[g + 1]] - rcu[gcu[g]],
+                         a.split_target);
+  };
+  if (ksplit) {
+    scan_into(ng, splits_of, a.split_cu, sh);
+    scan_into(
+        ng,
+        [&](int g) {
+          const int sg = splits_of(g);
+          return sg > 1 ? sg * (pcu[g + 1] - pcu[g]) : 0;
+        },
+        a.part_row, sh);
+    for (int g = t; g < ng; g += kMetaThreads) {
+      const int sg = a.split_cu[g + 1] - a.split_cu[g];
+      const int b0 = gcu[g];
+      const long long rows = (long long)rcu[gcu[g + 1]] - rcu[b0];
+      int i = b0;
+      for (int k = 0; k < sg; ++k) {
+        // first branch at or after i whose preceding rows reach k/sg of the
+        // group's rows, leaving one branch for every later split
+        const long long want = (rows * k + sg - 1) / sg;
+        const int last = gcu[g + 1] - (sg - k);
+        while (i < last && (long long)rcu[i] - rcu[b0] < want) ++i;
+        a.split_first[a.split_cu[g] + k] = i;
+        ++i;
+      }
+    }
+    __syncthreads();
+  }
+
   // Sources (segments that own tiles), their tile counts and ranking keys.
   // Replay key-stationary launches hold the prompt tiles of every group
-  // (they read all response rows of the group; ranked first) followed by
-  // the own-branch tiles.
+  // (ranked first) followed by the own-branch tiles.
   const int tq = a.tile_q;
   int nsrc;
   if (a.mode == kMetaQPrefill || a.mode == kMetaKPrefill) nsrc = ng;
@@ -89,8 +126,9 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(MetaArgs a) {
   };
   auto tiles_of = [&](int s) -> int {
     const int len = seg_len(s);
-    return (a.mode == kMetaQPrefill || a.mode == kMetaQReplay) ? ceil_div(len, tq)
-                                                              : ceil_div(len, kTileKV);
+    if (a.mode == kMetaQPrefill || a.mode == kMetaQReplay) return ceil_div(len, tq);
+    const int n = ceil_div(len, kTileKV);
+    return (ksplit && s < ng) ? n * (a.split_cu[s + 1] - a.split_cu[s]) : n;
   };
   auto key_of = [&](int s) -> int {
     if (a.mode == kMetaKReplay && s < ng) return (1 << 30) + (ng - s);
@@ -117,7 +155,7 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(MetaArgs a) {
   KItem* kout = static_cast<KItem*>(a.items);
   for (int i = n + t; i < a.cap; i += kMetaThreads) {  // never leave a stale slot
     if (qmode) qout[i] = QItem{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-    else kout[i] = KItem{0, 0, 0, 0, 0, 0, 0, 0};
+    else kout[i] = KItem{0, 0, 0, 0, 0, 0, 0, 0, 0};
   }
 
   for (int i = t; i < n; i += kMetaThreads) {
@@ -162,8 +200,9 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(MetaArgs a) {
       qout[i] = q;
     } else {
       // key tiles: the first tile of a causal segment is read by the most rows
-      const int tile = u;
+      int tile = u;
       KItem k;
+      k.prow = 0;
       if (a.mode == kMetaKPrefill) {
         const int plen = pcu[s + 1] - pcu[s];
         k.kpos = tile * kTileKV;
@@ -174,16 +213,21 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(MetaArgs a) {
         k.seg_hi = s + 1;
         k.causal = 1;
         k.cost = plen - k.kpos;
-      } else if (s < ng) {  // prompt tile in replay: every branch of the group
+      } else if (s < ng) {  // prompt tile in replay: the branches of one split
         const int plen = pcu[s + 1] - pcu[s];
+        const int ntile = ceil_div(plen, kTileKV);
+        const int sg = a.split_cu[s + 1] - a.split_cu[s];
+        const int split = tile / ntile;
+        tile -= split * ntile;
         k.kpos = tile * kTileKV;
         k.nk = min(kTileKV, plen - k.kpos);
         k.k0 = pcu[s] + k.kpos;
-        k.kind = 1;
-        k.seg_lo = gcu[s];
-        k.seg_hi = gcu[s + 1];
+        k.kind = sg > 1 ? 3 : 1;
+        k.seg_lo = sg > 1 ? a.split_first[a.split_cu[s] + split] : gcu[s];
+        k.seg_hi = split + 1 < sg ? a.split_first[a.split_cu[s] + split + 1] : gcu[s + 1];
         k.causal = 0;
-        k.cost = rcu[gcu[s + 1]] - rcu[gcu[s]];
+        k.cost = rcu[k.seg_hi] - rcu[k.seg_lo];
+        k.prow = a.part_row[s] + split * plen + k.kpos;
       } else {  // own-branch tile
         const int b = s - ng;
         const int rlen = rcu[b + 1] - rcu[b];
@@ -203,6 +247,45 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(MetaArgs a) {
 
 hipError_t launch_meta(const MetaArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(meta_kernel, dim3(1), dim3(kMetaThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ seed reduce
+//
+// Prompt seeds of split groups: the splits' partial sums added in split
+// order (deterministic).  One thread per 4 floats of a prompt token.
+__global__ __launch_bounds__(256) void seed_reduce_kernel(SeedReduceArgs a) {
+  const int per_tok = a.width / 4;
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (long long)a.tokens * per_tok) return;
+  const int t = (int)(idx / per_tok), c = (int)(idx % per_tok) * 4;
+  int lo = 0, hi = a.n_groups - 1;  // group of token t: last g with prompt_cu[g] <= t
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.prompt_cu[mid] <= t) lo = mid;
+    else hi = mid - 1;
+  }
+  const int g = lo;
+  const int sg = a.split_cu[g + 1] - a.split_cu[g];
+  if (sg <= 1) return;
+  const int plen = a.prompt_cu[g + 1] - a.prompt_cu[g];
+  const size_t r0 = (size_t)a.part_row[g] + (t - a.prompt_cu[g]);
+  f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < sg; ++k) {
+    const size_t o = (r0 + (size_t)k * plen) * a.width + c;
+    sk += *reinterpret_cast<const f32x4*>(a.part_k + o);
+    sv += *reinterpret_cast<const f32x4*>(a.part_v + o);
+  }
+  const size_t o = (size_t)t * a.width + c;
+  *reinterpret_cast<f32x4*>(a.dk_seed + o) = sk;
+  *reinterpret_cast<f32x4*>(a.dv_seed + o) = sv;
+}
+
+hipError_t launch_seed_reduce(const SeedReduceArgs& a, hipStream_t s) {
+  const long long n = (long long)a.tokens * (a.width / 4);
+  if (n == 0) return hipSuccess;
+  const int grid = (int)((n + 255) / 256);
+  hipLaunchKernelGGL(seed_reduce_kernel, dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

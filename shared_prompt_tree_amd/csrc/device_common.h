@@ -88,20 +88,21 @@ __device__ __forceinline__ void lds_frag(Frag<T>& f, const T* tile, int row, int
   }
 }
 
-// One global_load_lds_dwordx4: every lane copies 16 bytes from its own
-// global address to LDS byte (lds_wave_dst + 16 * lane), lds_wave_dst being
+// One global_load_lds_dwordx4: every lane copies the 16 bytes at
+// base + byte_off (base wave-uniform in scalar registers, byte_off a 32-bit
+// per-lane offset) to LDS byte (lds_wave_dst + 16 * lane), lds_wave_dst being
 // uniform across the wave (it goes through M0).  The instruction is issued
 // from inline assembly so the compiler does not treat it as a pending LDS
 // write and stall later LDS reads of other buffers on it; the caller waits
 // for completion (wait_vmem) before the barrier that publishes the data.
 // Memory reads return in issue order, so any wait the compiler places for
 // its own loads stays correct.
-__device__ __forceinline__ void dma_16(const void* src, void* lds_wave_dst) {
+__device__ __forceinline__ void dma_16(const void* base, uint32_t byte_off, void* lds_wave_dst) {
   const uint32_t lds = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_wave_dst);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(src), "s"(lds)
+               : "v"(byte_off), "s"(base), "s"(lds)
                : "m0");
 }
 
@@ -118,8 +119,8 @@ __host__ __device__ constexpr int tile_elems() {
 // writing chunk l of them.  Lanes that land on a padding chunk or in the
 // slack load a duplicate of a real chunk, so no lane is switched off.
 // Global addresses are the wave-uniform `base` plus row_off(r) + chunk
-// offset in elements (32-bit; the caller clamps rows past the end to a
-// valid row).  Completion is awaited with wait_vmem() before the barrier
+// offset in elements; the byte offset must fit in 32 bits (the host checks
+// the largest one) and the caller clamps rows past the end to a valid row.  Completion is awaited with wait_vmem() before the barrier
 // that publishes the tile.
 template <typename T, int ROWS, int NCH, int NT, typename RowOff>
 __device__ __forceinline__ void g2l_tile(T* tile, const T* base, RowOff row_off) {
@@ -135,8 +136,8 @@ __device__ __forceinline__ void g2l_tile(T* tile, const T* base, RowOff row_off)
       const int q = p / STRIDE;
       const int r = q < ROWS ? q : ROWS - 1;
       const int s = min(p - q * STRIDE, NCH - 1);
-      const uint32_t off = (uint32_t)row_off(r) + (uint32_t)(s * CH);
-      dma_16(base + off, tile + p0 * CH);
+      const uint32_t off = ((uint32_t)row_off(r) + (uint32_t)(s * CH)) * (uint32_t)sizeof(T);
+      dma_16(base, off, tile + p0 * CH);
     }
   }
 }
@@ -229,8 +230,10 @@ struct QItem {
 // [seg_lo, seg_hi) that read it.
 struct KItem {
   int k0, nk, kpos;      // first key token (global), keys, position in its segment
-  int kind;              // 0: write I/O dtype; 1: write float32 seeds; 2: I/O dtype + seeds
+  int kind;              // 0: write I/O dtype; 1: write float32 seeds; 2: I/O dtype + seeds;
+                         // 3: write float32 partial seeds at row prow
   int seg_lo, seg_hi, causal, cost;
+  int prow;              // kind 3: partial-seed row of key 0
 };
 
 constexpr int kTileQ = 256;  // query rows per workgroup (query-stationary)

@@ -32,8 +32,40 @@ struct MetaArgs {
   void* items;            // [cap] out, segment-major
   int cap;                // number of items the host computed
   int tile_q;             // query tokens per query-stationary tile
+  // Replay key-stationary lists only: the prompt tiles of a group are split
+  // into prompt_splits(...) ranges of its branches.
+  long long split_target; // rows one split should read at most (0: no split)
+  int32_t* split_cu;      // [n_groups + 1] out: prefix of splits per group
+  int32_t* split_first;   // [sum of splits] out: first branch of each split
+  int32_t* part_row;      // [n_groups + 1] out: first partial-seed row of a group
 };
 hipError_t launch_meta(const MetaArgs& a, hipStream_t s);
+
+// Splits of the prompt key tiles of a group with `branches` branches that
+// hold `rows` response tokens: enough that one split reads at most `target`
+// rows, at most one per branch, at least one.  Host and device use this same
+// rule.
+__host__ __device__ inline int prompt_splits(int branches, long long rows, long long target) {
+  if (branches <= 1 || target <= 0) return 1;
+  const long long s = (rows + target - 1) / target;
+  return (int)(s < 1 ? 1 : (s > branches ? branches : s));
+}
+
+// Sum of the partial prompt seeds of split groups:
+// seed[t] = sum_k part[part_row[g] + k * P_g + (t - prompt_cu[g])].
+struct SeedReduceArgs {
+  const float* part_k;
+  const float* part_v;
+  float* dk_seed;
+  float* dv_seed;
+  const int32_t* prompt_cu;
+  const int32_t* split_cu;
+  const int32_t* part_row;
+  int n_groups;
+  int tokens;  // prompt tokens
+  int width;   // hkv * d floats per token
+};
+hipError_t launch_seed_reduce(const SeedReduceArgs& a, hipStream_t s);
 
 // Transposed, padded copy: out[hg][d][perm(col)] with col = pad[s]*hp +
 // u*hp + j for token u of segment s and head hg*hp + j; padding columns are
@@ -112,6 +144,8 @@ struct DkvLaunch {
   void* dv;
   float* dk_seed;      // kind 1 output / kind 2 input [tokens][hkv][d] float32
   float* dv_seed;
+  float* part_k;       // kind 3 output: partial seeds [partial rows][hkv][d] float32
+  float* part_v;
   const void* items;
   int n_items;
   int hq, hkv, hp, d, dtype;

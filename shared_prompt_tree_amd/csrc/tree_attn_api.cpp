@@ -18,7 +18,7 @@
 #include <cstring>
 #include <vector>
 
-#include "../../include/tree_attn.h"
+#include "tree_attn.h"
 #include "device_common.h"
 #include "launch.h"
 
@@ -41,7 +41,16 @@ struct Shape {
   long long p_pad = 0, r_pad = 0;    // padded token totals
   long long q_items_prefill = 0, q_items_replay = 0;
   long long k_items_prefill = 0, k_items_replay = 0;
+  // replay key-stationary list: splits of the prompt tiles (prompt_splits)
+  long long split_target = 0;  // rows one prompt split should read at most
+  long long n_splits = 0;      // sum over groups of the splits
+  long long part_rows = 0;     // partial-seed rows of the split groups
 };
+
+// Key-stationary workgroups one launch should have in flight on the whole
+// GPU (two per compute unit of a 256-CU MI355X): a work item reading more
+// than the launch's total rows divided by this is worth splitting.
+constexpr long long kSplitSlots = 512;
 
 int validate_problem(const tree_attn_problem* p, bool need_device, Shape& s) {
   if (!p) return TREE_ATTN_ERR_INVALID;
@@ -84,17 +93,46 @@ int validate_problem(const tree_attn_problem* p, bool need_device, Shape& s) {
     s.q_items_prefill += ceil_div(len, s.tile_q);
     s.k_items_prefill += ceil_div(len, kTileKV);
   }
-  s.k_items_replay = s.k_items_prefill;
+  // Rows read by the replay key-stationary items (prompt tiles read every
+  // response row of their group, an own-branch tile the rows at or after
+  // it), the longest own-branch item, and from them the split target.
+  long long total = 0, longest = 0;
   for (int i = 0; i < nb; ++i) {
     const int len = p->resp_cu_h[i + 1] - p->resp_cu_h[i];
     s.r_pad += pad_len(len);
     s.q_items_replay += ceil_div(len, s.tile_q);
-    s.k_items_replay += ceil_div(len, kTileKV);
+    const long long n = ceil_div(len, kTileKV);
+    s.k_items_replay += n;
+    total += n * len - (long long)kTileKV * n * (n - 1) / 2;
+    longest = std::max<long long>(longest, len);
+  }
+  for (int g = 0; g < ng; ++g) {
+    const int plen = p->prompt_cu_h[g + 1] - p->prompt_cu_h[g];
+    const long long rows =
+        (long long)p->resp_cu_h[p->group_branch_cu_h[g + 1]] - p->resp_cu_h[p->group_branch_cu_h[g]];
+    total += (long long)ceil_div(plen, kTileKV) * rows;
+  }
+  s.split_target = std::max(longest, (total * s.hkv + kSplitSlots - 1) / kSplitSlots);
+  for (int g = 0; g < ng; ++g) {
+    const int plen = p->prompt_cu_h[g + 1] - p->prompt_cu_h[g];
+    const int branches = p->group_branch_cu_h[g + 1] - p->group_branch_cu_h[g];
+    const long long rows =
+        (long long)p->resp_cu_h[p->group_branch_cu_h[g + 1]] - p->resp_cu_h[p->group_branch_cu_h[g]];
+    const int sg = prompt_splits(branches, rows, s.split_target);
+    s.n_splits += sg;
+    s.k_items_replay += (long long)ceil_div(plen, kTileKV) * sg;
+    if (sg > 1) s.part_rows += (long long)sg * plen;
   }
   // every index the kernels form must fit in int32
   const long long lim = (1LL << 31) - 1;
   if (s.p_pad * s.hp > lim || s.r_pad * s.hp > lim) return TREE_ATTN_ERR_INVALID;
+  if (s.k_items_replay * s.hkv > lim || s.part_rows > lim)
+    return TREE_ATTN_ERR_INVALID;
   if ((s.p_tokens + s.r_tokens) * (long long)s.hq > lim) return TREE_ATTN_ERR_INVALID;
+  // tile copies address a head group's slice of a transposed copy with a
+  // 32-bit byte offset
+  const long long slice = (long long)s.d * std::max(s.p_pad, s.r_pad) * s.hp * (long long)s.esz;
+  if (slice > (long long)UINT32_MAX) return TREE_ATTN_ERR_INVALID;
   return TREE_ATTN_OK;
 }
 
@@ -116,6 +154,9 @@ struct MetaBufs {
   int32_t* branch_group;
   int32_t* src_cu;
   int32_t* src_order;
+  int32_t* split_cu;
+  int32_t* split_first;
+  int32_t* part_row;
   void* items;
 };
 
@@ -126,6 +167,9 @@ MetaBufs take_meta(Carve& c, const Shape& s, long long cap, size_t item_bytes) {
   m.branch_group = static_cast<int32_t*>(c.take((s.nb + 1) * sizeof(int32_t)));
   m.src_cu = static_cast<int32_t*>(c.take((s.ng + s.nb + 1) * sizeof(int32_t)));
   m.src_order = static_cast<int32_t*>(c.take((s.ng + s.nb + 1) * sizeof(int32_t)));
+  m.split_cu = static_cast<int32_t*>(c.take((s.ng + 1) * sizeof(int32_t)));
+  m.split_first = static_cast<int32_t*>(c.take((s.n_splits + 1) * sizeof(int32_t)));
+  m.part_row = static_cast<int32_t*>(c.take((s.ng + 1) * sizeof(int32_t)));
   m.items = c.take(std::max<long long>(cap, 1) * item_bytes);
   return m;
 }
@@ -141,6 +185,8 @@ struct Plan {
   void* qt = nullptr;     // Q^T  [hq/hp][d][pad*hp]
   void* dot = nullptr;    // dO^T
   float* delta = nullptr; // [hq][tokens]
+  float* part_k = nullptr;  // partial prompt seeds of split groups [part_rows][hkv][d]
+  float* part_v = nullptr;
   size_t bytes = 0;
 };
 
@@ -168,6 +214,11 @@ Plan make_plan(const Shape& s, int op, void* base) {
       pl.qt = c.take((size_t)s.hq * s.d * s.r_pad * e);
       pl.dot = c.take((size_t)s.hq * s.d * s.r_pad * e);
       pl.delta = static_cast<float*>(c.take((size_t)s.hq * s.r_tokens * sizeof(float)));
+      if (s.part_rows > 0) {
+        const size_t part = (size_t)s.part_rows * s.hkv * s.d * sizeof(float);
+        pl.part_k = static_cast<float*>(c.take(part));
+        pl.part_v = static_cast<float*>(c.take(part));
+      }
       break;
     case TREE_ATTN_OP_PREFILL_BWD:
       pl.mq = take_meta(c, s, s.q_items_prefill, sizeof(QItem));
@@ -232,6 +283,10 @@ hipError_t run_meta(const tree_attn_problem* p, const Shape& s, const MetaBufs& 
   a.items = m.items;
   a.cap = (int)cap;
   a.tile_q = s.tile_q;
+  a.split_target = mode == kMetaKReplay ? s.split_target : 0;
+  a.split_cu = m.split_cu;
+  a.split_first = m.split_first;
+  a.part_row = m.part_row;
   return launch_meta(a, st);
 }
 
@@ -433,6 +488,8 @@ int tree_attn_replay_bwd(const tree_attn_problem* problem, const void* k_p, cons
     k.dv = dv_r;
     k.dk_seed = dk_p_seed;
     k.dv_seed = dv_p_seed;
+    k.part_k = pl.part_k;
+    k.part_v = pl.part_v;
     k.items = pl.mk.items;
     k.n_items = (int)s.k_items_replay;
     k.hq = s.hq;
@@ -444,6 +501,20 @@ int tree_attn_replay_bwd(const tree_attn_problem* problem, const void* k_p, cons
     k.qt_stride = (int)(s.r_pad * s.hp);
     k.scale = problem->softmax_scale;
     TA_TRY(launch_dkv(k, st));
+    if (seeds && s.part_rows > 0) {
+      SeedReduceArgs r;
+      r.part_k = pl.part_k;
+      r.part_v = pl.part_v;
+      r.dk_seed = dk_p_seed;
+      r.dv_seed = dv_p_seed;
+      r.prompt_cu = problem->prompt_cu_d;
+      r.split_cu = pl.mk.split_cu;
+      r.part_row = pl.mk.part_row;
+      r.n_groups = s.ng;
+      r.tokens = (int)s.p_tokens;
+      r.width = s.hkv * s.d;
+      TA_TRY(launch_seed_reduce(r, st));
+    }
   }
   return TREE_ATTN_OK;
 }
@@ -518,6 +589,8 @@ int tree_attn_prefill_bwd(const tree_attn_problem* problem, const void* q_p, con
   k.dk = dk_p;
   k.dv = dv_p;
   k.dk_seed = const_cast<float*>(dk_p_seed);
+  k.part_k = nullptr;
+  k.part_v = nullptr;
   k.dv_seed = const_cast<float*>(dv_p_seed);
   k.items = pl.mk.items;
   k.n_items = (int)s.k_items_prefill;

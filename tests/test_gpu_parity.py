@@ -68,6 +68,16 @@ EDGE = {
     "MQA": wl.Tree([129], [[64, 65]], 8, 1, 128, "bf16"),
     "f32 head_dim 128": wl.Tree([150], [[40, 90]], 2, 1, 128, "f32"),
     "f32 GQA ragged": wl.Tree([70, 33], [[5, 64, 1], [100]], 4, 2, 64, "f32"),
+    # Prompt tiles split over branch ranges (partial seeds + ordered sum).
+    # Split rule: target = max(longest branch, ceil(rows read by all key
+    # tiles * Hkv / 512)); a group's prompt tiles get min(G, ceil(R_g /
+    # target)) splits.  Here: 6 splits of one branch each.
+    "split prompt tiles": wl.Tree([64], [[128] * 6], 2, 1, 64, "bf16"),
+    # Group 0 (R = 669 rows, target 300): 3 splits with an empty and a 5-row
+    # branch inside; group 1 is not split.
+    "split uneven groups": wl.Tree([300, 40], [[100, 5, 300, 0, 64, 200], [50, 60]], 4, 2, 128,
+                                   "bf16"),
+    "split f32": wl.Tree([64], [[64] * 5], 2, 1, 64, "f32"),
 }
 
 
@@ -102,15 +112,29 @@ def test_detached_prompt_seeds():
     compare(lib, ref, TOL["bf16"], names=("dq_p", "dk_p", "dv_p"), label="detached")
 
 
+def test_detached_prompt_seeds_split():
+    """Detached prompt where the prompt tiles would be split."""
+    tree = wl.Tree([64], [[128] * 6], 2, 1, 64, "bf16")
+    prob, t = make_case(tree, 10)
+    lib = run_library(prob, t, seeds=False)
+    prompt_only = wl.Tree(tree.prompt_lens, [[]], 2, 1, 64, "bf16")
+    ti = {k: v for k, v in t.items() if k.endswith("_p")}
+    for k in ("q_r", "k_r", "v_r", "do_r"):
+        ti[k] = t[k][:0]
+    ref = run_oracle(prompt_only, ti)
+    compare(lib, ref, TOL["bf16"], names=("dq_p", "dk_p", "dv_p"), label="detached split")
+
+
 def test_deterministic():
     """No atomics on any output: two runs are bit-identical."""
-    tree = wl.Tree([700], [[300, 129, 64]], 8, 2, 128, "bf16")
-    prob, t = make_case(tree, 3)
-    a = run_library(prob, t)
-    b = run_library(prob, t)
-    for k, v in a.items():
-        if v is not None:
-            assert torch.equal(v, b[k]), k
+    for tree in (wl.Tree([700], [[300, 129, 64]], 8, 2, 128, "bf16"),
+                 wl.Tree([64], [[128] * 6], 2, 1, 64, "bf16")):  # split prompt tiles
+        prob, t = make_case(tree, 3)
+        a = run_library(prob, t)
+        b = run_library(prob, t)
+        for k, v in a.items():
+            if v is not None:
+                assert torch.equal(v, b[k]), k
 
 
 def test_lse_merge_matches_oracle():
