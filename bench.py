@@ -201,6 +201,18 @@ def measure_workload(name, steps, warmup, flattened=True):
         "launches_per_step": 2, "ms_per_step": round(kern[dom], 4),
     }
     rep["kernel_tflops"] = {k: round(kflops[k] / (kern[k] * 1e-3) / 1e12, 2) for k in kern}
+    # forward (prefill + replay_fwd) and backward (replay_bwd + prefill_bwd)
+    # on their own useful FLOPs (4d and 10d per pair), and the whole step
+    # with 12d per pair (no recompute counted) beside the 14d convention
+    base = pairs["tree"] * hq * d
+    fwd_ms = part["prefill"] + part["replay_fwd"]
+    bwd_ms = part["replay_bwd"] + part["prefill_bwd"]
+    rep["phases"] = {}
+    for ph, pms, f in (("fwd", fwd_ms, 4), ("bwd", bwd_ms, 10)):
+        tf = base * f / (pms * 1e-3) / 1e12 if pms > 0 else 0.0
+        rep["phases"][ph] = {"ms": round(pms, 4), "useful_tflops": round(tf, 2),
+                             "pct_of_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}
+    rep["useful_tflops_12d"] = round(base * 12 / (ms * 1e-3) / 1e12, 2)
 
     if flattened:
         ftree = wl.flattened_tree(tree)
@@ -244,7 +256,7 @@ def measure_workload(name, steps, warmup, flattened=True):
 def cpu_baseline(tree, t, workers):
     """The float64 oracle on a bounded sample of the workload: for one query
     head per worker, the flattened (prompt, first branch) sequence of group 0,
-    evaluated on its last 8192 prompt rows and its first 512 response rows
+    evaluated on its last 16384 prompt rows and its first 512 response rows
     (the whole key range each), in a process pool."""
     import multiprocessing as mp
 
@@ -257,7 +269,7 @@ def cpu_baseline(tree, t, workers):
     P = int(tree.prompt_cu[1])
     r0, r1 = int(tree.resp_cu[i]), int(tree.resp_cu[i + 1])
     n_resp = min(512, r1 - r0)
-    rows = np.concatenate([np.arange(max(0, P - 8192), P), np.arange(P, P + n_resp)])
+    rows = np.concatenate([np.arange(max(0, P - 16384), P), np.arange(P, P + n_resp)])
     heads = list(range(min(workers, tree.hq)))
     seqs = []
     for h in heads:
@@ -415,6 +427,7 @@ def main():
             "pct_of_bf16_peak": round(100 * a["tflops"] / PEAK_BF16_TFLOPS, 2),
             "breakdown_ms": a["breakdown_ms"], "kernel_ms": a["kernel_ms"],
             "kernel_tflops": a["kernel_tflops"], "roofline": a["roofline"],
+            "phases": a["phases"], "useful_tflops_12d": a["useful_tflops_12d"],
             "flattened_baseline": a.get("flattened_baseline"), "config": a["config"],
         }
         print(f"[bench] {args.also}: {a['ms_per_step']:.2f} ms/step, {a['tflops']:.1f} TFLOP/s",
@@ -450,6 +463,8 @@ def main():
         "breakdown_ms": main_rep["breakdown_ms"],
         "kernel_ms": main_rep["kernel_ms"],
         "kernel_tflops": main_rep["kernel_tflops"],
+        "phases": main_rep["phases"],
+        "useful_tflops_12d": main_rep["useful_tflops_12d"],
         "roofline": main_rep["roofline"],
         "flattened_baseline": main_rep.get("flattened_baseline"),
         "cpu_baseline": cpu,
