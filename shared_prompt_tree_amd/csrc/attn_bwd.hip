@@ -240,8 +240,9 @@ struct DkvArgs {
 };
 
 // Key-stationary dK/dV.  A workgroup of NW = 8 waves owns 32 * NW keys of one
-// kv head; wave w owns keys [32w, 32w + 32).  With two waves per SIMD the
-// MFMA phase of one wave overlaps the exponentials of the other.  V of the
+// kv head; wave w owns keys [32w, 32w + 32).  Inside a wave the VALU work
+// of a query block (exponentials, dS) is issued between MFMAs that do not
+// depend on it; the second wave on each SIMD fills the remaining gaps.  V of the
 // wave's keys stays in registers; for bf16 the K tile stays in LDS for the
 // whole loop (registers would not fit two waves per SIMD), for float32 K
 // stays in registers.  Query blocks of 32 rows (Q, dO, Q^T, dO^T, LSE, D)
@@ -410,63 +411,94 @@ __global__ __launch_bounds__(512) void dkv_kernel(DkvArgs<T, D> a) {
     // nothing to it.
     const bool skip = !wave_has_keys || (it.causal && tok0 + tpb - 1 < wave_kmin);
     if (!skip) {
+      // Four MFMA phases; each VALU step runs beside MFMAs that do not
+      // depend on it:  S = Q K^T;  dP = dO V^T beside P = exp(S - LSE);
+      // dV += P^T dO beside dS = P (dP - D);  dK += dS^T Q.
+      // s: lane l, register jj -> query row 8*(jj/4) + 4*lh + jj%4, key lr.
       f32x16 s = f32x16{}, dp = f32x16{};
+      Frag<T> fa[2], fb[2];
+      // S = Q K^T (operand loads one step ahead)
+      auto sload = [&](int kk, int slot) {
+        lds_frag(fa[slot], qs, lr, QROW, 16 * kk + 8 * lh);
+        if constexpr (KLDS) lds_frag(fb[slot], ktile, krow, QROW, 16 * kk + 8 * lh);
+      };
+      sload(0, 0);
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        Frag<T> qa, ga, kb;
-        lds_frag(qa, qs, lr, QROW, 16 * kk + 8 * lh);
-        lds_frag(ga, gs, lr, QROW, 16 * kk + 8 * lh);
-        if constexpr (KLDS) {
-          lds_frag(kb, ktile, krow, QROW, 16 * kk + 8 * lh);
-          mma(s, qa, kb);
-        } else {
-          mma(s, qa, kf[kk]);
-        }
-        mma(dp, ga, vf[kk]);
+        if (kk + 1 < NKK) sload(kk + 1, (kk + 1) & 1);
+        if constexpr (KLDS) mma(s, fa[kk & 1], fb[kk & 1]);
+        else mma(s, fa[kk & 1], kf[kk]);
       }
-      // s: lane l, register jj -> query row 8*(jj/4) + 4*lh + jj%4, key lr.
       // Causal mask: row r (token tok0 + r/hp) is hidden from this lane's
       // key iff r < (key - tok0) * hp, i.e. 8*(jj/4) + jj%4 < row_lim.
       const bool need_mask = it.causal && (tok0 < wave_kmax);
       const int row_lim = (key_loc - tok0) * hp - 4 * lh;
-      auto grad_scores = [&](auto masked) {
+      auto body = [&](auto masked) {
+        f32x4 lv, dv;
+        // Phases 2-4 read one operand fragment per MFMA, from a stream of
+        // NKK dO, 2*NDB dO^T and 2*NDB Q^T fragments, loaded two steps ahead.
+        constexpr int NS = NKK + 4 * NDB;
+        Frag<T> fr[3];
+        auto oload = [&](int n) {
+          if (n >= NS) return;
+          Frag<T>& f = fr[n % 3];
+          if (n < NKK) lds_frag(f, gs, lr, QROW, 16 * n + 8 * lh);
+          else if (n < NKK + 2 * NDB) {
+            const int st = n - NKK;
+            lds_frag(f, tgs, 32 * (st >> 1) + lr, TROW, 16 * (st & 1) + 8 * lh);
+          } else {
+            const int st = n - NKK - 2 * NDB;
+            lds_frag(f, tqs, 32 * (st >> 1) + lr, TROW, 16 * (st & 1) + 8 * lh);
+          }
+        };
+        oload(0);
+        oload(1);
+        // dP = dO V^T beside P = exp(S * scale - LSE), two elements a step
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int r0 = 8 * g4 + 4 * lh;
-          const f32x4 lv = *reinterpret_cast<const f32x4*>(lse_s + r0);
-          const f32x4 dv = *reinterpret_cast<const f32x4*>(del_s + r0);
+        for (int kk = 0; kk < NKK; ++kk) {
+          oload(kk + 2);
+          mma(dp, fr[kk % 3], vf[kk]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int jj = 4 * g4 + e;
+          for (int u = 0; u < 16 / NKK; ++u) {
+            const int jj = kk * (16 / NKK) + u, g4 = jj >> 2, e = jj & 3;
+            if (e == 0) lv = *reinterpret_cast<const f32x4*>(lse_s + 8 * g4 + 4 * lh);
             float p = fast_exp2(s[jj] * c2 - lv[e]);
             if constexpr (decltype(masked)::value) {
               if (8 * g4 + e < row_lim) p = 0.f;
             }
             s[jj] = p;
-            dp[jj] = p * (dp[jj] - dv[e]);
           }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        Frag<T> pf[2], sf[2];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) to_frag(pf[hf], s, 8 * hf);
+        // dV += P^T dO beside dS = P (dP - D)
+#pragma unroll
+        for (int st = 0; st < 2 * NDB; ++st) {  // st = 2*db + hf
+          const int n = NKK + st;
+          oload(n + 2);
+          mma(dva[st >> 1], pf[st & 1], fr[n % 3]);
+#pragma unroll
+          for (int u = 0; u < 16 / (2 * NDB); ++u) {
+            const int jj = st * (16 / (2 * NDB)) + u, g4 = jj >> 2, e = jj & 3;
+            if (e == 0) dv = *reinterpret_cast<const f32x4*>(del_s + 8 * g4 + 4 * lh);
+            dp[jj] = s[jj] * (dp[jj] - dv[e]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) to_frag(sf[hf], dp, 8 * hf);
+        // dK += dS^T Q
+#pragma unroll
+        for (int st = 0; st < 2 * NDB; ++st) {
+          const int n = NKK + 2 * NDB + st;
+          oload(n + 2);
+          mma(dka[st >> 1], sf[st & 1], fr[n % 3]);
         }
       };
-      if (need_mask) grad_scores(std::true_type{});
-      else grad_scores(std::false_type{});
-      Frag<T> pf[2], sf[2];
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        to_frag(pf[hf], s, 8 * hf);
-        to_frag(sf[hf], dp, 8 * hf);
-      }
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int tr = 32 * db + lr;
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          Frag<T> gt, qt;
-          lds_frag(gt, tgs, tr, TROW, 16 * hf + 8 * lh);
-          lds_frag(qt, tqs, tr, TROW, 16 * hf + 8 * lh);
-          mma(dva[db], pf[hf], gt);
-          mma(dka[db], sf[hf], qt);
-        }
-      }
+      if (need_mask) body(std::true_type{});
+      else body(std::false_type{});
     }
     if (more) lstore(stage ^ 1);
     wait_vmem();

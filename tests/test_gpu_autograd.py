@@ -189,8 +189,9 @@ def test_multilayer_gradients_match_flattened(dtype_name):
     loss.backward()
     torch.cuda.synchronize()
 
-    lerr = abs(float(loss) - float(ref_loss)) / abs(float(ref_loss))
-    say(f"[autograd] {dtype_name}: loss {float(loss):.6f} vs {float(ref_loss):.6f} "
+    lv, rv = float(loss.detach()), float(ref_loss.detach())
+    lerr = abs(lv - rv) / abs(rv)
+    say(f"[autograd] {dtype_name}: loss {lv:.6f} vs {rv:.6f} "
         f"(rel {lerr:.2e})")
     assert lerr <= tol
     worst = 0.0
