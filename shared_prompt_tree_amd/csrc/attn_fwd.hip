@@ -2,7 +2,8 @@
 // replay (AugTree paper, section 3.2, "Shared prompt prefill pass" and
 // "Response replay"; tile semantics of section 2.2 / Fig. 3).
 //
-// One workgroup = 8 waves = 256 query rows of one head group.  A row is a
+// One workgroup = 8 waves = 256 query rows of one head group (or, bf16 with
+// enough work, 12 waves = 384 rows, three waves per SIMD).  A row is a
 // (token, head) pair: the hp query heads of a token that share one kv head
 // are packed next to each other, so every K/V tile staged in LDS feeds all of
 // them (GQA reuse).  Each wave owns 32 rows and keeps their Q in registers.
@@ -43,9 +44,9 @@ struct FwdArgs {
   float scale_log2;
 };
 
-template <typename T, int D>
-__global__ __launch_bounds__(512) void fwd_kernel(FwdArgs<T, D> a) {
-  constexpr int NT = 512, KT = kTileK, CH = ChunkOf<T>::kElems;
+template <typename T, int D, int NW>
+__global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs<T, D> a) {
+  constexpr int NT = 64 * NW, KT = kTileK, CH = ChunkOf<T>::kElems;
   constexpr int NCHK = D / CH;        // 16-byte chunks per K row
   constexpr int NCHV = KT / CH;       // chunks per V^T row
   constexpr int KROW = tile_row_elems<T, NCHK>();  // padded row lengths
@@ -223,7 +224,7 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdArgs<T, D> a) {
         lt > 0.f ? (m_run + fast_log2(lt)) * kLn2 : -INFINITY;
 }
 
-template <typename T, int D>
+template <typename T, int D, int NW>
 static hipError_t launch_fwd_t(const FwdLaunch& l, hipStream_t s) {
   FwdArgs<T, D> a;
   a.q = static_cast<const T*>(l.q);
@@ -246,23 +247,25 @@ static hipError_t launch_fwd_t(const FwdLaunch& l, hipStream_t s) {
   constexpr int CH = 16 / sizeof(T);
   const size_t smem =
       2 * sizeof(T) * (size_t)(tile_elems<T, kTileK, D / CH>() + tile_elems<T, D, kTileK / CH>());
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fwd_kernel<T, D>),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fwd_kernel<T, D, NW>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
   const int grid = xcd_grid(l.n_items, a.n_hg);
   if (grid <= 0) return hipSuccess;
   hipEvent_t e0, e1;
   kernel_events(kKernelFwd, &e0, &e1);
-  if (e0) hipExtLaunchKernelGGL(fwd_kernel<T, D>, dim3(grid), dim3(512), smem, s, e0, e1, 0, a);
-  else fwd_kernel<T, D><<<dim3(grid), dim3(512), smem, s>>>(a);
+  if (e0) hipExtLaunchKernelGGL(fwd_kernel<T, D, NW>, dim3(grid), dim3(64 * NW), smem, s, e0, e1, 0, a);
+  else fwd_kernel<T, D, NW><<<dim3(grid), dim3(64 * NW), smem, s>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd(const FwdLaunch& l, hipStream_t s) {
   if (l.dtype == 1) {
-    return l.d == 128 ? launch_fwd_t<bf16, 128>(l, s) : launch_fwd_t<bf16, 64>(l, s);
+    if (l.waves == 12)
+      return l.d == 128 ? launch_fwd_t<bf16, 128, 12>(l, s) : launch_fwd_t<bf16, 64, 12>(l, s);
+    return l.d == 128 ? launch_fwd_t<bf16, 128, 8>(l, s) : launch_fwd_t<bf16, 64, 8>(l, s);
   }
-  return l.d == 128 ? launch_fwd_t<float, 128>(l, s) : launch_fwd_t<float, 64>(l, s);
+  return l.d == 128 ? launch_fwd_t<float, 128, 8>(l, s) : launch_fwd_t<float, 64, 8>(l, s);
 }
 
 }  // namespace treeattn

@@ -237,6 +237,10 @@ struct KItem {
 };
 
 constexpr int kTileQ = 256;  // query rows per workgroup (query-stationary)
+// The bf16 forward kernel also runs as 12 waves (384 query rows, three waves
+// per SIMD) where that tiling still gives every CU several workgroups.
+constexpr int kTileQWide = 384;
+constexpr int kWideMinWorkgroups = 4 * 256;
 constexpr int kTileK = 64;   // keys per step (query-stationary)
 constexpr int kTileKV = 256; // keys per workgroup (key-stationary)
 constexpr int kBlockQ = 64;  // query rows per step (key-stationary)

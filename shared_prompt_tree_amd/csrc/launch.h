@@ -103,6 +103,7 @@ struct FwdLaunch {
   int lse_stride;
   int vt_a_stride, vt_b_stride;
   float scale;
+  int waves;  // 8 (256 query rows per item) or 12 (384, bf16 only)
 };
 hipError_t launch_fwd(const FwdLaunch& a, hipStream_t s);
 

@@ -40,6 +40,7 @@ struct Shape {
   long long p_tokens = 0, r_tokens = 0;
   long long p_pad = 0, r_pad = 0;    // padded token totals
   long long q_items_prefill = 0, q_items_replay = 0;
+  long long wq_items_prefill = 0, wq_items_replay = 0;  // with 384-row forward tiles
   long long k_items_prefill = 0, k_items_replay = 0;
   // replay key-stationary list: splits of the prompt tiles (prompt_splits)
   long long split_target = 0;  // rows one prompt split should read at most
@@ -91,6 +92,7 @@ int validate_problem(const tree_attn_problem* p, bool need_device, Shape& s) {
     const int len = p->prompt_cu_h[g + 1] - p->prompt_cu_h[g];
     s.p_pad += pad_len(len);
     s.q_items_prefill += ceil_div(len, s.tile_q);
+    s.wq_items_prefill += ceil_div(len, kTileQWide / s.hp);
     s.k_items_prefill += ceil_div(len, kTileKV);
   }
   // Rows read by the replay key-stationary items (prompt tiles read every
@@ -101,6 +103,7 @@ int validate_problem(const tree_attn_problem* p, bool need_device, Shape& s) {
     const int len = p->resp_cu_h[i + 1] - p->resp_cu_h[i];
     s.r_pad += pad_len(len);
     s.q_items_replay += ceil_div(len, s.tile_q);
+    s.wq_items_replay += ceil_div(len, kTileQWide / s.hp);
     const long long n = ceil_div(len, kTileKV);
     s.k_items_replay += n;
     total += n * len - (long long)kTileKV * n * (n - 1) / 2;
@@ -267,7 +270,7 @@ int hip_status(hipError_t e) {
   } while (0)
 
 hipError_t run_meta(const tree_attn_problem* p, const Shape& s, const MetaBufs& m, int mode,
-                    long long cap, hipStream_t st) {
+                    long long cap, hipStream_t st, int tile_q = 0) {
   MetaArgs a;
   a.mode = mode;
   a.n_groups = s.ng;
@@ -282,7 +285,7 @@ hipError_t run_meta(const tree_attn_problem* p, const Shape& s, const MetaBufs& 
   a.src_order = m.src_order;
   a.items = m.items;
   a.cap = (int)cap;
-  a.tile_q = s.tile_q;
+  a.tile_q = tile_q > 0 ? tile_q : s.tile_q;
   a.split_target = mode == kMetaKReplay ? s.split_target : 0;
   a.split_cu = m.split_cu;
   a.split_first = m.split_first;
@@ -304,6 +307,18 @@ hipError_t run_transpose(const void* in, void* out, int heads, int hp, const Sha
   t.seg_pad = seg_pad_d;
   t.pad_tokens = (int)pad_tokens;
   return launch_transpose(t, s.dtype, st);
+}
+
+// Forward launch shape: the 12-wave kernel (384 rows per item) where its
+// item count still gives every CU several workgroups, else 8 waves.
+struct FwdShape {
+  int waves, tile_q;
+  long long items;
+};
+FwdShape fwd_shape(const Shape& s, long long items, long long wide_items) {
+  if (s.dtype == TREE_ATTN_BF16 && wide_items * (s.hq / s.hp) >= kWideMinWorkgroups)
+    return {12, kTileQWide / s.hp, wide_items};
+  return {8, s.tile_q, items};
 }
 
 }  // namespace
@@ -341,10 +356,12 @@ int tree_attn_prefill(const tree_attn_problem* problem, const void* q_p, const v
   if (s.p_tokens == 0) return TREE_ATTN_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  TA_TRY(run_meta(problem, s, pl.mq, kMetaQPrefill, s.q_items_prefill, st));
+  const FwdShape fs = fwd_shape(s, s.q_items_prefill, s.wq_items_prefill);
+  TA_TRY(run_meta(problem, s, pl.mq, kMetaQPrefill, s.q_items_prefill, st, fs.tile_q));
   TA_TRY(run_transpose(v_p, pl.vt_p, s.hkv, 1, s, s.ng, problem->prompt_cu_d, pl.mq.prompt_pad,
                        s.p_pad, st));
   FwdLaunch f;
+  f.waves = fs.waves;
   f.q = q_p;
   f.o = o_p;
   f.lse = lse_p;
@@ -353,7 +370,7 @@ int tree_attn_prefill(const tree_attn_problem* problem, const void* q_p, const v
   f.k_b = k_p;
   f.vt_b = pl.vt_p;
   f.items = pl.mq.items;
-  f.n_items = (int)s.q_items_prefill;
+  f.n_items = (int)fs.items;
   f.hq = s.hq;
   f.hkv = s.hkv;
   f.hp = s.hp;
@@ -382,12 +399,14 @@ int tree_attn_replay_fwd(const tree_attn_problem* problem, const void* k_p, cons
   if (s.r_tokens == 0) return TREE_ATTN_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  TA_TRY(run_meta(problem, s, pl.mq, kMetaQReplay, s.q_items_replay, st));
+  const FwdShape fs = fwd_shape(s, s.q_items_replay, s.wq_items_replay);
+  TA_TRY(run_meta(problem, s, pl.mq, kMetaQReplay, s.q_items_replay, st, fs.tile_q));
   TA_TRY(run_transpose(v_p, pl.vt_p, s.hkv, 1, s, s.ng, problem->prompt_cu_d, pl.mq.prompt_pad,
                        s.p_pad, st));
   TA_TRY(run_transpose(v_r, pl.vt_r, s.hkv, 1, s, s.nb, problem->resp_cu_d, pl.mq.resp_pad,
                        s.r_pad, st));
   FwdLaunch f;
+  f.waves = fs.waves;
   f.q = q_r;
   f.o = o_r;
   f.lse = lse_r;
@@ -396,7 +415,7 @@ int tree_attn_replay_fwd(const tree_attn_problem* problem, const void* k_p, cons
   f.k_b = k_r;
   f.vt_b = pl.vt_r;
   f.items = pl.mq.items;
-  f.n_items = (int)s.q_items_replay;
+  f.n_items = (int)fs.items;
   f.hq = s.hq;
   f.hkv = s.hkv;
   f.hp = s.hp;

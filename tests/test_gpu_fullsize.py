@@ -181,3 +181,35 @@ def test_full_size(name):
     say(f"[full] {name} sum rules: |sum dK|/|dK| {worst_k:.2e}, "
         f"|sum dV - sum dO|/|sum dO| {worst_v:.2e}")
     assert worst_k <= TOL["bf16"] and worst_v <= TOL["bf16"]
+
+
+def test_wide_forward_tiles():
+    """Prefill large enough for the 12-wave forward kernel (384-row tiles:
+    6144 tokens x 16 packed heads / 384 = 256 tiles per head group, 4 head
+    groups): sampled prompt rows of O, LSE and dQ against the oracle, and
+    the sum rules."""
+    tree = wl.Tree([6144], [[700]], 64, 4, 64, "bf16")
+    scale = 1.0 / math.sqrt(tree.d)
+    say("[wide] prefill 6144 tokens, 64/4 heads, d 64")
+    prob, t = make_case(tree, 21)
+    lib = run_library(prob, t)
+    rng = np.random.default_rng(21)
+    P = 6144
+    got = {k: [] for k in ("o", "lse", "dq")}
+    want = {k: [] for k in got}
+    for h in (0, 17, 63):
+        f = _flat(tree, t, 0, 0, h, with_branch=False)
+        loc = np.array(sorted({0, 383, 384, P - 1, *rng.integers(0, P, size=12).tolist()}))
+        o, lse, dq, _, _ = oracle.causal_unit(f["q"], f["k"], f["v"], f["do"], scale, rows=loc)
+        got["o"].append(host64(lib["o_p"][loc, h]))
+        got["lse"].append(host64(lib["lse_p"][h, loc]))
+        got["dq"].append(host64(lib["dq_p"][loc, h]))
+        want["o"].append(o)
+        want["lse"].append(lse)
+        want["dq"].append(dq)
+    for k in got:
+        a = np.concatenate([x.ravel() for x in got[k]])
+        b = np.concatenate([x.ravel() for x in want[k]])
+        err = rel_l2(a, b)
+        say(f"[wide] sampled {k}: {len(a)} values, rel L2 {err:.2e}")
+        assert err <= TOL["bf16"], (k, err)
