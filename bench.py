@@ -336,6 +336,8 @@ def summarize(dirs, command):
             name = r["Name"]
             short = next((k for k, v in KERNEL_SYMBOLS.items() if v in name), None)
             label = short or name.split("(")[0][:26]
+            if short == "fwd":  # the 12-wave and 8-wave launches of the forward kernel
+                label += " (12 waves)" if ("Li12E" in name or ", 12>" in name) else " (8 waves)"
             lines.append(f"{label:26s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e6:8.3f} "
                          f"{float(r['TotalDurationNs']) / 1e6:10.3f}  {float(r['Percentage']):5.1f}%")
     counters = {}
