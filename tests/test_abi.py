@@ -73,6 +73,37 @@ def test_invalid_problem_rejected(kw, code):
     assert e.value.code == code
 
 
+def test_transposed_copy_offset_limit():
+    """A head group's slice of a transposed copy is addressed with 32-bit
+    byte offsets: head_dim * padded tokens * packed heads * element size must
+    stay below 4 GiB (16 packed heads here: 64 query heads on 4 kv heads)."""
+    d, hp, esz = 64, 16, 2
+    ok = (2 ** 32 - 1) // (d * hp * esz) // 64 * 64   # largest padded prompt that fits
+    p = small_problem(prompt_cu=[0, ok], group_branch_cu=[0, 0], resp_cu=[0],
+                      num_q_heads=64, num_kv_heads=4, head_dim=d)
+    assert ops.tree_attn_workspace_size(p, ops.OP_PREFILL) > 0
+    p = small_problem(prompt_cu=[0, ok + 64], group_branch_cu=[0, 0], resp_cu=[0],
+                      num_q_heads=64, num_kv_heads=4, head_dim=d)
+    with pytest.raises(ops.TreeAttnError) as e:
+        ops.tree_attn_workspace_size(p, ops.OP_PREFILL)
+    assert e.value.code == -1
+
+
+def test_replay_workspace_holds_split_partial_seeds():
+    """A short prompt read by many long branches is split over branch ranges
+    (one split per branch here: 6 branches of 128 rows, target = the longest
+    branch), so the replay-backward workspace holds float32 partial seeds for
+    6 x 64 prompt rows (dK and dV); a single branch of the same total length
+    is never split."""
+    kw = dict(prompt_cu=[0, 64], group_branch_cu=[0, 6], resp_cu=[0, 128, 256, 384, 512, 640, 768],
+              num_q_heads=2, num_kv_heads=1, head_dim=64)
+    split = ops.tree_attn_workspace_size(small_problem(**kw), ops.OP_REPLAY_BWD)
+    kw.update(group_branch_cu=[0, 1], resp_cu=[0, 768])
+    single = ops.tree_attn_workspace_size(small_problem(**kw), ops.OP_REPLAY_BWD)
+    partial = 2 * 6 * 64 * 1 * 64 * 4
+    assert partial <= split - single < partial + 64 * 1024
+
+
 def test_bad_op_and_null_out_pointer():
     lib = ops.library()
     p = small_problem()
