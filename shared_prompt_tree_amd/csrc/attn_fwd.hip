@@ -165,33 +165,75 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs<T, D> a) {
       m_run = m_new;
     }
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-    float ps = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int jj = 0; jj < 16; ++jj) {
+    if constexpr (NW == 12) {
+      // Three waves per SIMD: P of keys 0-31, then its products with V, the
+      // exponentials of keys 32-63 issued between those products (they do
+      // not depend on them), then the products of keys 32-63.  (With two
+      // waves per SIMD the plain order below is faster.)
+      float ps = 0.f;
+      auto expo = [&](int kb, int jj) {
         const float p = fast_exp2(s[kb][jj] * c2 - m_use);
         s[kb][jj] = p;
         ps += p;
+      };
+      Frag<T> pf[2][2];
+      Frag<T> vf[2];
+      auto vload = [&](int kb, int step, int slot) {  // step = 2*db + hf
+        const int db = step >> 1, hf = step & 1;
+        lds_frag(vf[slot], vt, 32 * db + lr, VROW, 16 * (2 * kb + hf) + 8 * lh);
+      };
+      vload(0, 0, 0);
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) expo(0, jj);
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) to_frag(pf[0][hf], s[0], 8 * hf);
+#pragma unroll
+      for (int step = 0; step < 2 * NDB; ++step) {
+        if (step + 1 < 2 * NDB) vload(0, step + 1, (step + 1) & 1);
+        else vload(1, 0, (step + 1) & 1);
+        mma(oacc[step >> 1], vf[step & 1], pf[0][step & 1]);
+#pragma unroll
+        for (int u = 0; u < 16 / (2 * NDB); ++u) expo(1, step * (16 / (2 * NDB)) + u);
+        __builtin_amdgcn_sched_barrier(0);
       }
-    lsum += ps;
-
-    Frag<T> pf[2][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int hf = 0; hf < 2; ++hf) to_frag(pf[1][hf], s[1], 8 * hf);
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) to_frag(pf[kb][hf], s[kb], 8 * hf);
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const int vr = 32 * db + lr;
+      for (int step = 0; step < 2 * NDB; ++step) {
+        const int slot = (2 * NDB + step) & 1;
+        if (step + 1 < 2 * NDB) vload(1, step + 1, slot ^ 1);
+        mma(oacc[step >> 1], vf[slot], pf[1][step & 1]);
+      }
+      lsum += ps;
+    } else {
+      float ps = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          Frag<T> vf;
-          lds_frag(vf, vt, vr, VROW, 16 * (2 * kb + hf) + 8 * lh);
-          mma(oacc[db], vf, pf[kb][hf]);
+        for (int jj = 0; jj < 16; ++jj) {
+          const float p = fast_exp2(s[kb][jj] * c2 - m_use);
+          s[kb][jj] = p;
+          ps += p;
         }
+      lsum += ps;
+
+      Frag<T> pf[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) to_frag(pf[kb][hf], s[kb], 8 * hf);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int vr = 32 * db + lr;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            Frag<T> vf;
+            lds_frag(vf, vt, vr, VROW, 16 * (2 * kb + hf) + 8 * lh);
+            mma(oacc[db], vf, pf[kb][hf]);
+          }
+      }
     }
 
     wait_vmem();
