@@ -156,16 +156,23 @@ __global__ __launch_bounds__(512) void dq_kernel(DqArgs<T, D> a) {
     const bool inA = j < na;
     const int kst0 = (inA ? j : j - na) * KT;
     const bool need_mask = inA ? (kst0 + KT > it.alen) : (kst0 + KT - 1 > it.qpos + wave_tok0);
-    const int lim = inA ? it.alen - 1 : it.qpos + tok;
+    // Causal mask, only on tiles that cross it: hidden scores become -inf,
+    // so their P is exactly 0 below.
+    if (need_mask) {
+      const int lim = inA ? it.alen - 1 : it.qpos + tok;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) {
+          const int key = kst0 + 32 * kb + 8 * (jj >> 2) + 4 * lh + (jj & 3);
+          if (key > lim) s[kb][jj] = -INFINITY;
+        }
+    }
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj) {
-        float p = fast_exp2(s[kb][jj] * c2 - lse2);
-        if (need_mask) {
-          const int key = kst0 + 32 * kb + 8 * (jj >> 2) + 4 * lh + (jj & 3);
-          if (key > lim) p = 0.f;
-        }
+        const float p = fast_exp2(s[kb][jj] * c2 - lse2);
         s[kb][jj] = p * (dp[kb][jj] - dl);
       }
     Frag<T> sf[KB][2];
