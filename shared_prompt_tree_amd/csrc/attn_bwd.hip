@@ -22,7 +22,6 @@
 // segment B (causal).  It recomputes P and dP per tile and accumulates
 // dQ^T += K^T dS^T with K^T read from a pre-transposed copy.
 #include <hip/hip_ext.h>
-#include <type_traits>
 
 #include "device_common.h"
 #include "launch.h"
@@ -436,11 +435,17 @@ __global__ __launch_bounds__(512) void dkv_kernel(DkvArgs<T, D> a) {
         if constexpr (KLDS) mma(s, fa[kk & 1], fb[kk & 1]);
         else mma(s, fa[kk & 1], kf[kk]);
       }
-      // Causal mask: row r (token tok0 + r/hp) is hidden from this lane's
-      // key iff r < (key - tok0) * hp, i.e. 8*(jj/4) + jj%4 < row_lim.
-      const bool need_mask = it.causal && (tok0 < wave_kmax);
-      const int row_lim = (key_loc - tok0) * hp - 4 * lh;
-      auto body = [&](auto masked) {
+      // Causal mask, only on blocks that cross it: row r (token tok0 + r/hp)
+      // is hidden from this lane's key iff r < (key - tok0) * hp, i.e.
+      // 8*(jj/4) + jj%4 < row_lim; hidden scores become -inf, so their P
+      // (and dS) is exactly 0 below.
+      if (it.causal && tok0 < wave_kmax) {
+        const int row_lim = (key_loc - tok0) * hp - 4 * lh;
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj)
+          if (8 * (jj >> 2) + (jj & 3) < row_lim) s[jj] = -INFINITY;
+      }
+      {
         f32x4 lv, dv;
         // Phases 2-4 read one operand fragment per MFMA, from a stream of
         // NKK dO, 2*NDB dO^T and 2*NDB Q^T fragments, loaded two steps ahead.
@@ -469,11 +474,7 @@ __global__ __launch_bounds__(512) void dkv_kernel(DkvArgs<T, D> a) {
           for (int u = 0; u < 16 / NKK; ++u) {
             const int jj = kk * (16 / NKK) + u, g4 = jj >> 2, e = jj & 3;
             if (e == 0) lv = *reinterpret_cast<const f32x4*>(lse_s + 8 * g4 + 4 * lh);
-            float p = fast_exp2(s[jj] * c2 - lv[e]);
-            if constexpr (decltype(masked)::value) {
-              if (8 * g4 + e < row_lim) p = 0.f;
-            }
-            s[jj] = p;
+            s[jj] = fast_exp2(s[jj] * c2 - lv[e]);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -503,9 +504,7 @@ __global__ __launch_bounds__(512) void dkv_kernel(DkvArgs<T, D> a) {
           oload(n + 2);
           mma(dka[st >> 1], sf[st & 1], fr[n % 3]);
         }
-      };
-      if (need_mask) body(std::true_type{});
-      else body(std::false_type{});
+      }
     }
     if (more) lstore(stage ^ 1);
     wait_vmem();
