@@ -384,6 +384,19 @@ def summarize(dirs, command):
                 v = sum(float(r["Counter_Value"]) for r in other[c] if sym in r["Kernel_Name"])
                 row.append(f"{c}={v:.4g}")
             lines.append(f"{kind}: " + " ".join(row))
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in other and "GRBM_GUI_ACTIVE" in other:
+            # GRBM_GUI_ACTIVE sums the active cycles of the 8 XCDs; each of the
+            # 1024 SIMDs can keep its matrix unit busy for all of them.
+            lines.append("")
+            lines.append("MFMA busy share of SIMD cycles while the GPU was active "
+                         "(SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 * 1024)):")
+            for kind, sym in KERNEL_SYMBOLS.items():
+                busy = sum(float(r["Counter_Value"]) for r in other["SQ_VALU_MFMA_BUSY_CYCLES"]
+                           if sym in r["Kernel_Name"])
+                act = sum(float(r["Counter_Value"]) for r in other["GRBM_GUI_ACTIVE"]
+                          if sym in r["Kernel_Name"])
+                if act > 0:
+                    lines.append(f"{kind}: {busy / (act / 8 * 1024):.3f}")
     head = ["rocprofv3 summary", f"command: {command}", ""]
     return "\n".join(head + lines) + "\n"
 
