@@ -49,6 +49,7 @@ struct DqArgs {
   int lse_stride;
   int kt_a_stride, kt_b_stride;
   float scale_log2, scale;
+  float* dq_part;  // split prompt column: [chunks][tokens][hq][D] float32, or null
 };
 
 // KB 32-key blocks per step: 2 (64 keys), or 1 where two double-buffered
@@ -196,6 +197,21 @@ __global__ __launch_bounds__(512) void dq_kernel(DqArgs<T, D> a) {
   }
 
   if (!qvalid) return;
+  if (a.dq_part != nullptr) {
+    // one chunk of a split prompt column: its float32 share of dQ
+    float* prow = a.dq_part +
+                  (((size_t)it.chunk * a.lse_stride + it.q0 + tok) * a.hq + head) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[db][4 * g4 + e] * a.scale;
+        *reinterpret_cast<f32x4*>(prow + 32 * db + 8 * g4 + 4 * lh) = v;
+      }
+    return;
+  }
   T* drow = a.dq + ((size_t)(it.q0 + tok) * a.hq + head) * D;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
@@ -571,6 +587,7 @@ static hipError_t launch_dq_t(const DqLaunch& l, hipStream_t s) {
   a.kt_b_stride = l.kt_b_stride;
   a.scale_log2 = l.scale * kLog2e;
   a.scale = l.scale;
+  a.dq_part = l.dq_part;
   constexpr int CH = 16 / sizeof(T);
   const size_t smem = 2 * sizeof(T) *
                       (size_t)(2 * tile_elems<T, 32 * KB, D / CH>() + tile_elems<T, D, 32 * KB / CH>());

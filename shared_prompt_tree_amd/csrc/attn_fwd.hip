@@ -42,6 +42,8 @@ struct FwdArgs {
   int lse_stride;
   int vt_a_stride, vt_b_stride;
   float scale_log2;
+  float* o_part;    // split prompt column: [chunks][tokens][hq][D] float32, or null
+  float* lse_part;  // [chunks][hq][tokens]
 };
 
 template <typename T, int D, int NW>
@@ -243,6 +245,24 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs<T, D> a) {
   const float lt = sum_with_other_half(lsum);
   if (!qvalid) return;
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const float lse = lt > 0.f ? (m_run + fast_log2(lt)) * kLn2 : -INFINITY;
+  if (a.o_part != nullptr) {
+    // one chunk of a split prompt column: float32 partial state (O, LSE),
+    // merged afterwards
+    const size_t tokens = a.lse_stride;
+    float* orow = a.o_part + (((size_t)it.chunk * tokens + it.q0 + tok) * a.hq + head) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = oacc[db][4 * g4 + e] * inv;
+        *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * g4 + 4 * lh) = v;
+      }
+    if (lh == 0) a.lse_part[((size_t)it.chunk * a.hq + head) * tokens + it.q0 + tok] = lse;
+    return;
+  }
   T* orow = a.o + ((size_t)(it.q0 + tok) * a.hq + head) * D;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
@@ -261,9 +281,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs<T, D> a) {
         *reinterpret_cast<f32x4*>(orow + d0) = v;
       }
     }
-  if (lh == 0)
-    a.lse[(size_t)head * a.lse_stride + it.q0 + tok] =
-        lt > 0.f ? (m_run + fast_log2(lt)) * kLn2 : -INFINITY;
+  if (lh == 0) a.lse[(size_t)head * a.lse_stride + it.q0 + tok] = lse;
 }
 
 template <typename T, int D, int NW>
@@ -286,6 +304,8 @@ static hipError_t launch_fwd_t(const FwdLaunch& l, hipStream_t s) {
   a.vt_a_stride = l.vt_a_stride;
   a.vt_b_stride = l.vt_b_stride;
   a.scale_log2 = l.scale * kLog2e;
+  a.o_part = l.o_part;
+  a.lse_part = l.lse_part;
   constexpr int CH = 16 / sizeof(T);
   const size_t smem =
       2 * sizeof(T) * (size_t)(tile_elems<T, kTileK, D / CH>() + tile_elems<T, D, kTileK / CH>());

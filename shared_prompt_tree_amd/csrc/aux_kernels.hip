@@ -126,7 +126,8 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(MetaArgs a) {
   };
   auto tiles_of = [&](int s) -> int {
     const int len = seg_len(s);
-    if (a.mode == kMetaQPrefill || a.mode == kMetaQReplay) return ceil_div(len, tq);
+    if (a.mode == kMetaQPrefill) return ceil_div(len, tq);
+    if (a.mode == kMetaQReplay) return ceil_div(len, tq) * a.col_splits;
     const int n = ceil_div(len, kTileKV);
     return (ksplit && s < ng) ? n * (a.split_cu[s + 1] - a.split_cu[s]) : n;
   };
@@ -154,7 +155,7 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(MetaArgs a) {
   QItem* qout = static_cast<QItem*>(a.items);
   KItem* kout = static_cast<KItem*>(a.items);
   for (int i = n + t; i < a.cap; i += kMetaThreads) {  // never leave a stale slot
-    if (qmode) qout[i] = QItem{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    if (qmode) qout[i] = QItem{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};  // nq = 0: no work
     else kout[i] = KItem{0, 0, 0, 0, 0, 0, 0, 0, 0};
   }
 
@@ -168,10 +169,14 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(MetaArgs a) {
     const int s = a.src_order[lo];
     const int u = i - a.src_cu[lo];
     if (qmode) {
-      // query tiles: the last tile of a causal segment reads the most keys
-      const int tile = tiles_of(s) - 1 - u;
+      // query tiles: the last tile of a causal segment reads the most keys;
+      // a split replay list holds the col_splits chunks of a tile in a row
+      const int nsplit = a.mode == kMetaQReplay ? a.col_splits : 1;
+      const int chunk = u % nsplit;
+      const int tile = tiles_of(s) / nsplit - 1 - u / nsplit;
       QItem q;
-      q.r0 = q.r1 = 0;
+      q.chunk = chunk;
+      q.pad_ = 0;
       if (a.mode == kMetaQPrefill) {
         const int plen = pcu[s + 1] - pcu[s];
         q.qpos = tile * tq;
@@ -189,11 +194,16 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(MetaArgs a) {
         q.qpos = tile * tq;
         q.nq = min(tq, rlen - q.qpos);
         q.q0 = rcu[s] + q.qpos;
-        q.a0 = pcu[g];
-        q.alen = pcu[g + 1] - pcu[g];
-        q.apad = a.prompt_pad[g];
+        // prompt chunk [k0, k1) in whole 64-key tiles
+        const int plen = pcu[g + 1] - pcu[g];
+        const int ptiles = ceil_div(plen, kTileK);
+        const int k0 = min(plen, (int)((long long)ptiles * chunk / nsplit) * kTileK);
+        const int k1 = min(plen, (int)((long long)ptiles * (chunk + 1) / nsplit) * kTileK);
+        q.a0 = pcu[g] + k0;
+        q.alen = k1 - k0;
+        q.apad = a.prompt_pad[g] + k0;
         q.b0 = rcu[s];
-        q.blen = q.qpos + q.nq;
+        q.blen = chunk == nsplit - 1 ? q.qpos + q.nq : 0;
         q.bpad = a.resp_pad[s];
       }
       q.cost = ceil_div(q.alen, kTileK) + ceil_div(q.blen, kTileK);
@@ -279,6 +289,36 @@ __global__ __launch_bounds__(256) void seed_reduce_kernel(SeedReduceArgs a) {
   const size_t o = (size_t)t * a.width + c;
   *reinterpret_cast<f32x4*>(a.dk_seed + o) = sk;
   *reinterpret_cast<f32x4*>(a.dv_seed + o) = sv;
+}
+
+// ------------------------------------------------------------ chunk sums
+//
+// dQ of a split replay launch: the chunks' float32 shares added in chunk
+// order (deterministic), written in the output dtype.  One thread per 4
+// elements.
+template <typename T>
+__global__ __launch_bounds__(256) void sum_parts_kernel(const float* in, int parts, long long n,
+                                                        T* out) {
+  const long long i = ((long long)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (i >= n) return;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < parts; ++k) acc += *reinterpret_cast<const f32x4*>(in + k * n + i);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) out[i + e] = static_cast<T>(acc[e]);
+}
+
+hipError_t launch_sum_parts(const float* in, int parts, long long n, void* out, int dtype,
+                            hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const long long threads = n / 4;
+  const int grid = (int)((threads + 255) / 256);
+  if (dtype == 1)
+    hipLaunchKernelGGL(sum_parts_kernel<bf16>, dim3(grid), dim3(256), 0, s, in, parts, n,
+                       static_cast<bf16*>(out));
+  else
+    hipLaunchKernelGGL(sum_parts_kernel<float>, dim3(grid), dim3(256), 0, s, in, parts, n,
+                       static_cast<float*>(out));
+  return hipGetLastError();
 }
 
 hipError_t launch_seed_reduce(const SeedReduceArgs& a, hipStream_t s) {

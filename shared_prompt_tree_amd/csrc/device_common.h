@@ -223,7 +223,9 @@ struct QItem {
   int q0, nq, qpos;      // first query token (global), tokens in tile, position in B
   int a0, alen, apad;    // segment A: first key token, keys, padded offset
   int b0, blen, bpad;    // segment B: first key token, keys read, padded offset
-  int cost, r0, r1;
+  int cost;
+  int chunk;             // prompt-column chunk of a split replay launch (else 0)
+  int pad_;
 };
 
 // Key-stationary item: a tile of key tokens and the query segments

@@ -32,6 +32,10 @@ struct MetaArgs {
   void* items;            // [cap] out, segment-major
   int cap;                // number of items the host computed
   int tile_q;             // query tokens per query-stationary tile
+  // Replay query-stationary lists only: the prompt column of every query
+  // tile is cut into col_splits chunks of whole 64-key tiles (1: not split);
+  // the last chunk also holds the row's own branch.
+  int col_splits;
   // Replay key-stationary lists only: the prompt tiles of a group are split
   // into prompt_splits(...) ranges of its branches.
   long long split_target; // rows one split should read at most (0: no split)
@@ -104,6 +108,10 @@ struct FwdLaunch {
   int vt_a_stride, vt_b_stride;
   float scale;
   int waves;  // 8 (256 query rows per item) or 12 (384, bf16 only)
+  // Split prompt column: each item writes its chunk's normalised O (float32,
+  // [chunks][tokens][hq][d]) and LSE ([chunks][hq][tokens]) instead of o/lse.
+  float* o_part;   // null: not split
+  float* lse_part;
 };
 hipError_t launch_fwd(const FwdLaunch& a, hipStream_t s);
 
@@ -125,8 +133,16 @@ struct DqLaunch {
   int lse_stride;
   int kt_a_stride, kt_b_stride;
   float scale;
+  // Split prompt column: each item writes its chunk's dQ share (float32,
+  // [chunks][tokens][hq][d]) instead of dq.
+  float* dq_part;  // null: not split
 };
 hipError_t launch_dq(const DqLaunch& a, hipStream_t s);
+
+// out[i] = sum over k < parts of in[k * n + i], in the output dtype (0 float32,
+// 1 bf16); the chunk partial sums of a split dQ.
+hipError_t launch_sum_parts(const float* in, int parts, long long n, void* out, int dtype,
+                            hipStream_t s);
 
 struct DkvLaunch {
   const void* k;       // own-branch keys (kind 0 tiles) [tokens][hkv][d]

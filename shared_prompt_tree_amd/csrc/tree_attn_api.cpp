@@ -46,12 +46,21 @@ struct Shape {
   long long split_target = 0;  // rows one prompt split should read at most
   long long n_splits = 0;      // sum over groups of the splits
   long long part_rows = 0;     // partial-seed rows of the split groups
+  int max_prompt = 0;          // longest prompt
+  int col_splits = 1;          // prompt-column chunks of the replay query lists
 };
 
 // Key-stationary workgroups one launch should have in flight on the whole
 // GPU (two per compute unit of a 256-CU MI355X): a work item reading more
 // than the launch's total rows divided by this is worth splitting.
 constexpr long long kSplitSlots = 512;
+
+// Replay query-stationary launches (forward, dQ) with fewer workgroups than
+// this cut each prompt column into chunks (each at least kMinChunkKeys keys)
+// until they have about this many; the chunks' partial results are merged.
+constexpr long long kColFill = 512;
+constexpr int kMinChunkKeys = 1024;
+constexpr int kMaxColSplits = 64;
 
 int validate_problem(const tree_attn_problem* p, bool need_device, Shape& s) {
   if (!p) return TREE_ATTN_ERR_INVALID;
@@ -90,6 +99,7 @@ int validate_problem(const tree_attn_problem* p, bool need_device, Shape& s) {
   s.r_tokens = p->resp_cu_h[nb];
   for (int g = 0; g < ng; ++g) {
     const int len = p->prompt_cu_h[g + 1] - p->prompt_cu_h[g];
+    s.max_prompt = std::max(s.max_prompt, len);
     s.p_pad += pad_len(len);
     s.q_items_prefill += ceil_div(len, s.tile_q);
     s.wq_items_prefill += ceil_div(len, kTileQWide / s.hp);
@@ -131,6 +141,12 @@ int validate_problem(const tree_attn_problem* p, bool need_device, Shape& s) {
   if (s.p_pad * s.hp > lim || s.r_pad * s.hp > lim) return TREE_ATTN_ERR_INVALID;
   if (s.k_items_replay * s.hkv > lim || s.part_rows > lim)
     return TREE_ATTN_ERR_INVALID;
+  const long long q_wgs = s.q_items_replay * (s.hq / s.hp);
+  if (q_wgs > 0 && q_wgs < kColFill) {
+    const long long by_fill = (kColFill + q_wgs - 1) / q_wgs;
+    const long long by_len = s.max_prompt / kMinChunkKeys;
+    s.col_splits = (int)std::max(1LL, std::min({by_fill, by_len, (long long)kMaxColSplits}));
+  }
   if ((s.p_tokens + s.r_tokens) * (long long)s.hq > lim) return TREE_ATTN_ERR_INVALID;
   // tile copies address a head group's slice of a transposed copy with a
   // 32-bit byte offset
@@ -190,6 +206,9 @@ struct Plan {
   float* delta = nullptr; // [hq][tokens]
   float* part_k = nullptr;  // partial prompt seeds of split groups [part_rows][hkv][d]
   float* part_v = nullptr;
+  float* o_part = nullptr;    // split prompt column: [chunks][r_tokens][hq][d]
+  float* lse_part = nullptr;  // [chunks][hq][r_tokens]
+  float* dq_part = nullptr;   // [chunks][r_tokens][hq][d]
   size_t bytes = 0;
 };
 
@@ -205,12 +224,21 @@ Plan make_plan(const Shape& s, int op, void* base) {
       pl.vt_p = c.take(kvT_p);
       break;
     case TREE_ATTN_OP_REPLAY_FWD:
-      pl.mq = take_meta(c, s, s.q_items_replay, sizeof(QItem));
+      pl.mq = take_meta(c, s, s.q_items_replay * s.col_splits, sizeof(QItem));
       pl.vt_p = c.take(kvT_p);
       pl.vt_r = c.take(kvT_r);
+      if (s.col_splits > 1) {
+        pl.o_part = static_cast<float*>(
+            c.take((size_t)s.col_splits * s.r_tokens * s.hq * s.d * sizeof(float)));
+        pl.lse_part = static_cast<float*>(
+            c.take((size_t)s.col_splits * s.hq * s.r_tokens * sizeof(float)));
+      }
       break;
     case TREE_ATTN_OP_REPLAY_BWD:
-      pl.mq = take_meta(c, s, s.q_items_replay, sizeof(QItem));
+      pl.mq = take_meta(c, s, s.q_items_replay * s.col_splits, sizeof(QItem));
+      if (s.col_splits > 1)
+        pl.dq_part = static_cast<float*>(
+            c.take((size_t)s.col_splits * s.r_tokens * s.hq * s.d * sizeof(float)));
       pl.mk = take_meta(c, s, s.k_items_replay, sizeof(KItem));
       pl.kt_p = c.take(kvT_p);
       pl.kt_r = c.take(kvT_r);
@@ -286,6 +314,7 @@ hipError_t run_meta(const tree_attn_problem* p, const Shape& s, const MetaBufs& 
   a.items = m.items;
   a.cap = (int)cap;
   a.tile_q = tile_q > 0 ? tile_q : s.tile_q;
+  a.col_splits = mode == kMetaQReplay ? s.col_splits : 1;
   a.split_target = mode == kMetaKReplay ? s.split_target : 0;
   a.split_cu = m.split_cu;
   a.split_first = m.split_first;
@@ -362,6 +391,8 @@ int tree_attn_prefill(const tree_attn_problem* problem, const void* q_p, const v
                        s.p_pad, st));
   FwdLaunch f;
   f.waves = fs.waves;
+  f.o_part = nullptr;
+  f.lse_part = nullptr;
   f.q = q_p;
   f.o = o_p;
   f.lse = lse_p;
@@ -399,8 +430,11 @@ int tree_attn_replay_fwd(const tree_attn_problem* problem, const void* k_p, cons
   if (s.r_tokens == 0) return TREE_ATTN_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  const FwdShape fs = fwd_shape(s, s.q_items_replay, s.wq_items_replay);
-  TA_TRY(run_meta(problem, s, pl.mq, kMetaQReplay, s.q_items_replay, st, fs.tile_q));
+  const bool split = s.col_splits > 1;
+  const FwdShape fs = split ? FwdShape{8, s.tile_q, s.q_items_replay * s.col_splits}
+                            : fwd_shape(s, s.q_items_replay, s.wq_items_replay);
+  TA_TRY(run_meta(problem, s, pl.mq, kMetaQReplay, s.q_items_replay * s.col_splits, st,
+                  fs.tile_q));
   TA_TRY(run_transpose(v_p, pl.vt_p, s.hkv, 1, s, s.ng, problem->prompt_cu_d, pl.mq.prompt_pad,
                        s.p_pad, st));
   TA_TRY(run_transpose(v_r, pl.vt_r, s.hkv, 1, s, s.nb, problem->resp_cu_d, pl.mq.resp_pad,
@@ -425,7 +459,12 @@ int tree_attn_replay_fwd(const tree_attn_problem* problem, const void* k_p, cons
   f.vt_a_stride = (int)s.p_pad;
   f.vt_b_stride = (int)s.r_pad;
   f.scale = problem->softmax_scale;
+  f.o_part = pl.o_part;
+  f.lse_part = pl.lse_part;
   TA_TRY(launch_fwd(f, st));
+  if (split)  // the chunks' partial states, merged (section 3.3)
+    TA_TRY(launch_lse_merge(s.col_splits, (int)s.r_tokens, s.hq, s.d, s.dtype, pl.o_part,
+                            pl.lse_part, o_r, lse_r, st));
   return TREE_ATTN_OK;
 }
 
@@ -453,7 +492,7 @@ int tree_attn_replay_bwd(const tree_attn_problem* problem, const void* k_p, cons
   (void)hipGetLastError();
   // K-stationary list first: it also writes both padded offset arrays.
   TA_TRY(run_meta(problem, s, pl.mk, kMetaKReplay, s.k_items_replay, st));
-  TA_TRY(run_meta(problem, s, pl.mq, kMetaQReplay, s.q_items_replay, st));
+  TA_TRY(run_meta(problem, s, pl.mq, kMetaQReplay, s.q_items_replay * s.col_splits, st));
   if (s.r_tokens > 0) {
     TA_TRY(launch_row_dot(do_r, o_r, pl.delta, (int)s.r_tokens, s.hq, s.d, s.dtype, st));
     TA_TRY(run_transpose(k_p, pl.kt_p, s.hkv, 1, s, s.ng, problem->prompt_cu_d,
@@ -477,7 +516,8 @@ int tree_attn_replay_bwd(const tree_attn_problem* problem, const void* k_p, cons
     q.v_b = v_r;
     q.kt_b = pl.kt_r;
     q.items = pl.mq.items;
-    q.n_items = (int)s.q_items_replay;
+    q.n_items = (int)(s.q_items_replay * s.col_splits);
+    q.dq_part = pl.dq_part;
     q.hq = s.hq;
     q.hkv = s.hkv;
     q.hp = s.hp;
@@ -488,6 +528,9 @@ int tree_attn_replay_bwd(const tree_attn_problem* problem, const void* k_p, cons
     q.kt_b_stride = (int)s.r_pad;
     q.scale = problem->softmax_scale;
     TA_TRY(launch_dq(q, st));
+    if (pl.dq_part)
+      TA_TRY(launch_sum_parts(pl.dq_part, s.col_splits, s.r_tokens * s.hq * s.d, dq_r, s.dtype,
+                              st));
   }
   if (s.r_tokens > 0 || (seeds && s.p_tokens > 0)) {
     DkvLaunch k;
@@ -582,6 +625,7 @@ int tree_attn_prefill_bwd(const tree_attn_problem* problem, const void* q_p, con
   q.kt_b = pl.kt_p;
   q.items = pl.mq.items;
   q.n_items = (int)s.q_items_prefill;
+  q.dq_part = nullptr;
   q.hq = s.hq;
   q.hkv = s.hkv;
   q.hp = s.hp;

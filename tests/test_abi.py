@@ -104,6 +104,20 @@ def test_replay_workspace_holds_split_partial_seeds():
     assert partial <= split - single < partial + 64 * 1024
 
 
+def test_replay_workspace_holds_prompt_column_partials():
+    """Few response rows behind a long prompt: 4 query workgroups (8 heads
+    packed 4 per kv head, 2 branches of one tile) -> the prompt column is cut
+    into min(ceil(512 / 4), 8192 // 1024) = 8 chunks, whose float32 partial
+    O (and LSE) the replay-forward workspace holds."""
+    kw = dict(prompt_cu=[0, 8192], group_branch_cu=[0, 2], resp_cu=[0, 40, 73],
+              num_q_heads=8, num_kv_heads=2, head_dim=128)
+    split = ops.tree_attn_workspace_size(small_problem(**kw), ops.OP_REPLAY_FWD)
+    kw.update(prompt_cu=[0, 1000])  # too short to cut
+    whole = ops.tree_attn_workspace_size(small_problem(**kw), ops.OP_REPLAY_FWD)
+    partial = 8 * 73 * 8 * 128 * 4 + 8 * 8 * 73 * 4
+    assert split - whole >= partial
+
+
 def test_bad_op_and_null_out_pointer():
     lib = ops.library()
     p = small_problem()

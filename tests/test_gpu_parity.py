@@ -78,6 +78,16 @@ EDGE = {
     "split uneven groups": wl.Tree([300, 40], [[100, 5, 300, 0, 64, 200], [50, 60]], 4, 2, 128,
                                    "bf16"),
     "split f32": wl.Tree([64], [[64] * 5], 2, 1, 64, "f32"),
+    # Few response rows behind a long prompt: the replay query lists cut the
+    # prompt column into chunks until the launch has ~512 workgroups, each
+    # chunk >= 1024 keys; forward partials merged by lse_merge, dQ partials
+    # summed.  4 workgroups -> 8 chunks of 1024 keys here.
+    "split prompt column": wl.Tree([8192], [[40, 33]], 8, 2, 128, "bf16"),
+    # 6 workgroups -> 4 chunks; prompts of 47 and 79 tiles, an empty branch.
+    "split prompt column, two groups": wl.Tree([3000, 5000], [[17, 0, 64], [100]], 4, 2, 64,
+                                               "bf16"),
+    # 1 workgroup -> 4 chunks of 1024 keys, float32.
+    "split prompt column f32": wl.Tree([4096], [[20]], 2, 1, 64, "f32"),
 }
 
 
