@@ -126,6 +126,13 @@ __global__ __launch_bounds__(512) void dq_kernel(DqArgs<T, D> a) {
   f32x16 acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+  // The dP accumulators start at -D of this lane's row, so the products give
+  // dP - D directly.  (float32 at head_dim 128 has no 16 registers to spare
+  // for the starting block and subtracts D afterwards.)
+  constexpr bool kNegD = !(sizeof(T) == 4 && D == 128);
+  f32x16 negd;
+#pragma unroll
+  for (int jj = 0; jj < 16; ++jj) negd[jj] = kNegD ? -dl : 0.f;
   const float c2 = a.scale_log2;
   const int wave_tok0 = (32 * w) / a.hp;
 
@@ -142,7 +149,7 @@ __global__ __launch_bounds__(512) void dq_kernel(DqArgs<T, D> a) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       s[kb] = f32x16{};
-      dp[kb] = f32x16{};
+      dp[kb] = negd;
       const int kr = 32 * kb + lr;
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
@@ -173,7 +180,7 @@ __global__ __launch_bounds__(512) void dq_kernel(DqArgs<T, D> a) {
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj) {
         const float p = fast_exp2(s[kb][jj] * c2 - lse2);
-        s[kb][jj] = p * (dp[kb][jj] - dl);
+        s[kb][jj] = p * (kNegD ? dp[kb][jj] : dp[kb][jj] - dl);
       }
     Frag<T> sf[KB][2];
 #pragma unroll
@@ -383,12 +390,13 @@ __global__ __launch_bounds__(512) void dkv_kernel(DkvArgs<T, D> a) {
       lst = tid < QB ? a.lse[li] : a.delta[li];
     }
   };
-  // LSE is kept as LSE * log2(e); rows past the segment get LSE = +inf
-  // (P = 0) and D = 0.
+  // LSE is kept as LSE * log2(e) and D as -D (the starting value of the
+  // dP accumulator, so the products give dP - D); rows past the segment get
+  // LSE = +inf (P = 0) and D = 0.
   auto lstore = [&](int stage) {
     if (tid < 2 * QB)
       fsm[stage * 2 * QB + tid] =
-          tid < QB ? (lvalid ? lst * kLog2e : INFINITY) : (lvalid ? lst : 0.f);
+          tid < QB ? (lvalid ? lst * kLog2e : INFINITY) : (lvalid ? -lst : 0.f);
   };
 
   f32x16 dka[NDB], dva[NDB];
@@ -462,7 +470,15 @@ __global__ __launch_bounds__(512) void dkv_kernel(DkvArgs<T, D> a) {
           if (8 * (jj >> 2) + (jj & 3) < row_lim) s[jj] = -INFINITY;
       }
       {
-        f32x4 lv, dv;
+        f32x4 lv;
+        // dp starts at -D of its query rows (row 8*g4 + 4*lh + e in
+        // register 4*g4 + e)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4 nd = *reinterpret_cast<const f32x4*>(del_s + 8 * g4 + 4 * lh);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dp[4 * g4 + e] = nd[e];
+        }
         // Phases 2-4 read one operand fragment per MFMA, from a stream of
         // NKK dO, 2*NDB dO^T and 2*NDB Q^T fragments, loaded two steps ahead.
         constexpr int NS = NKK + 4 * NDB;
@@ -497,7 +513,7 @@ __global__ __launch_bounds__(512) void dkv_kernel(DkvArgs<T, D> a) {
         Frag<T> pf[2], sf[2];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) to_frag(pf[hf], s, 8 * hf);
-        // dV += P^T dO beside dS = P (dP - D)
+        // dV += P^T dO beside dS = P (dP - D), dp holding dP - D
 #pragma unroll
         for (int st = 0; st < 2 * NDB; ++st) {  // st = 2*db + hf
           const int n = NKK + st;
@@ -505,9 +521,8 @@ __global__ __launch_bounds__(512) void dkv_kernel(DkvArgs<T, D> a) {
           mma(dva[st >> 1], pf[st & 1], fr[n % 3]);
 #pragma unroll
           for (int u = 0; u < 16 / (2 * NDB); ++u) {
-            const int jj = st * (16 / (2 * NDB)) + u, g4 = jj >> 2, e = jj & 3;
-            if (e == 0) dv = *reinterpret_cast<const f32x4*>(del_s + 8 * g4 + 4 * lh);
-            dp[jj] = s[jj] * (dp[jj] - dv[e]);
+            const int jj = st * (16 / (2 * NDB)) + u;
+            dp[jj] = s[jj] * dp[jj];
           }
           __builtin_amdgcn_sched_barrier(0);
         }

@@ -109,7 +109,10 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs<T, D> a) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
   float m_run = -INFINITY;  // running max of scaled scores, log2 units
-  float lsum = 0.f;         // this lane's share of the running normaliser
+  // This lane's share of the running normaliser.  It sums the probabilities
+  // as rounded for the P.V product (exact for float32 I/O), so the output
+  // is a weighted mean of V rows with weights that sum to one.
+  float lsum = 0.f;
   const float c2 = a.scale_log2;
   const int wave_tok0 = (32 * w) / a.hp;  // smallest token index of this wave
 
@@ -173,11 +176,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs<T, D> a) {
       // not depend on them), then the products of keys 32-63.  (With two
       // waves per SIMD the plain order below is faster.)
       float ps = 0.f;
-      auto expo = [&](int kb, int jj) {
-        const float p = fast_exp2(s[kb][jj] * c2 - m_use);
-        s[kb][jj] = p;
-        ps += p;
-      };
+      auto expo = [&](int kb, int jj) { s[kb][jj] = fast_exp2(s[kb][jj] * c2 - m_use); };
       Frag<T> pf[2][2];
       Frag<T> vf[2];
       auto vload = [&](int kb, int step, int slot) {  // step = 2*db + hf
@@ -188,7 +187,10 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs<T, D> a) {
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj) expo(0, jj);
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) to_frag(pf[0][hf], s[0], 8 * hf);
+      for (int hf = 0; hf < 2; ++hf) {
+        to_frag(pf[0][hf], s[0], 8 * hf);
+        ps = frag_sum(pf[0][hf], ps);
+      }
 #pragma unroll
       for (int step = 0; step < 2 * NDB; ++step) {
         if (step + 1 < 2 * NDB) vload(0, step + 1, (step + 1) & 1);
@@ -199,7 +201,10 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs<T, D> a) {
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) to_frag(pf[1][hf], s[1], 8 * hf);
+      for (int hf = 0; hf < 2; ++hf) {
+        to_frag(pf[1][hf], s[1], 8 * hf);
+        ps = frag_sum(pf[1][hf], ps);
+      }
 #pragma unroll
       for (int step = 0; step < 2 * NDB; ++step) {
         const int slot = (2 * NDB + step) & 1;
@@ -212,18 +217,17 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs<T, D> a) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int jj = 0; jj < 16; ++jj) {
-          const float p = fast_exp2(s[kb][jj] * c2 - m_use);
-          s[kb][jj] = p;
-          ps += p;
-        }
-      lsum += ps;
+        for (int jj = 0; jj < 16; ++jj) s[kb][jj] = fast_exp2(s[kb][jj] * c2 - m_use);
 
       Frag<T> pf[2][2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) to_frag(pf[kb][hf], s[kb], 8 * hf);
+        for (int hf = 0; hf < 2; ++hf) {
+          to_frag(pf[kb][hf], s[kb], 8 * hf);
+          ps = frag_sum(pf[kb][hf], ps);
+        }
+      lsum += ps;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         const int vr = 32 * db + lr;

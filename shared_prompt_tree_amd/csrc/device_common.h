@@ -91,15 +91,14 @@ __device__ __forceinline__ void lds_frag(Frag<T>& f, const T* tile, int row, int
 // One global_load_lds_dwordx4: every lane copies the 16 bytes at
 // base + byte_off (base wave-uniform in scalar registers, byte_off a 32-bit
 // per-lane offset) to LDS byte (lds_wave_dst + 16 * lane), lds_wave_dst being
-// uniform across the wave (it goes through M0).  The instruction is issued
+// a 32-bit LDS byte address uniform across the wave (it goes through M0).  The instruction is issued
 // from inline assembly so the compiler does not treat it as a pending LDS
 // write and stall later LDS reads of other buffers on it; the caller waits
 // for completion (wait_vmem) before the barrier that publishes the data.
 // Memory reads return in issue order, so any wait the compiler places for
 // its own loads stays correct.
-__device__ __forceinline__ void dma_16(const void* base, uint32_t byte_off, void* lds_wave_dst) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_wave_dst);
+__device__ __forceinline__ void dma_16(const void* base, uint32_t byte_off, uint32_t lds_wave_dst) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_wave_dst);
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                :
                : "v"(byte_off), "s"(base), "s"(lds)
@@ -128,6 +127,9 @@ __device__ __forceinline__ void g2l_tile(T* tile, const T* base, RowOff row_off)
   constexpr int STRIDE = NCH + 1;
   constexpr int NCHUNK = tile_elems<T, ROWS, NCH>() / CH;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // The low 32 bits of a generic pointer into LDS are the LDS address;
+  // taking them directly keeps the destination arithmetic 32-bit.
+  const uint32_t tile_lds = (uint32_t)(uintptr_t)tile;
 #pragma unroll
   for (int i = 0; i < (NCHUNK + NT - 1) / NT; ++i) {
     const int p0 = i * NT + 64 * w;  // first chunk of this wave instruction
@@ -137,7 +139,7 @@ __device__ __forceinline__ void g2l_tile(T* tile, const T* base, RowOff row_off)
       const int r = q < ROWS ? q : ROWS - 1;
       const int s = min(p - q * STRIDE, NCH - 1);
       const uint32_t off = ((uint32_t)row_off(r) + (uint32_t)(s * CH)) * (uint32_t)sizeof(T);
-      dma_16(base, off, tile + p0 * CH);
+      dma_16(base, off, tile_lds + (uint32_t)p0 * 16u);
     }
   }
 }
@@ -155,6 +157,23 @@ __device__ __forceinline__ void to_frag(Frag<bf16>& f, const f32x16& c, int j0) 
 __device__ __forceinline__ void to_frag(Frag<float>& f, const f32x16& c, int j0) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) f.v[e] = c[j0 + e];
+}
+
+// acc plus the sum of a fragment's 8 values.  For bf16, v_dot2 with a (1, 1)
+// operand adds two values per instruction (the sum then matches the
+// rounded probabilities that the P.V product uses).
+__device__ __forceinline__ float frag_sum(const Frag<bf16>& f, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {static_cast<bf16>(1.f), static_cast<bf16>(1.f)};
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{f.v[2 * e], f.v[2 * e + 1]}, one, acc, false);
+  return acc;
+}
+__device__ __forceinline__ float frag_sum(const Frag<float>& f, float acc) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc += f.v[e];
+  return acc;
 }
 
 __device__ __forceinline__ float to_f32(bf16 x) { return static_cast<float>(x); }
