@@ -138,7 +138,8 @@ def test_detached_prompt_seeds_split():
 def test_deterministic():
     """No atomics on any output: two runs are bit-identical."""
     for tree in (wl.Tree([700], [[300, 129, 64]], 8, 2, 128, "bf16"),
-                 wl.Tree([64], [[128] * 6], 2, 1, 64, "bf16")):  # split prompt tiles
+                 wl.Tree([64], [[128] * 6], 2, 1, 64, "bf16"),  # split prompt tiles
+                 wl.Tree([8192], [[40, 33]], 8, 2, 128, "bf16")):  # split prompt column
         prob, t = make_case(tree, 3)
         a = run_library(prob, t)
         b = run_library(prob, t)
