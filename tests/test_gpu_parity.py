@@ -66,6 +66,11 @@ EDGE = {
     "MHA head_dim 64": wl.Tree([300], [[100, 257]], 3, 3, 64, "bf16"),
     "GQA 7:1 (Qwen2.5-7B grouping)": wl.Tree([260], [[90, 130]], 14, 2, 128, "bf16"),
     "MQA": wl.Tree([129], [[64, 65]], 8, 1, 128, "bf16"),
+    # 16 query heads packed per kv head in a 32-row block (2 tokens a block),
+    # the largest packing; 12:1 packs 4 and leaves 3 head sub-groups.
+    "GQA 16:1": wl.Tree([300], [[100, 65]], 32, 2, 128, "bf16"),
+    "GQA 12:1 head_dim 64": wl.Tree([200], [[64, 90]], 24, 2, 64, "bf16"),
+    "GQA 32:1": wl.Tree([150, 70], [[33], [0, 9]], 32, 1, 128, "bf16"),
     "f32 head_dim 128": wl.Tree([150], [[40, 90]], 2, 1, 128, "f32"),
     "f32 GQA ragged": wl.Tree([70, 33], [[5, 64, 1], [100]], 4, 2, 64, "f32"),
     # Prompt tiles split over branch ranges (partial seeds + ordered sum).
