@@ -414,8 +414,8 @@ def main():
         print(summarize(args.summarize, args.summarize_command), end="")
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        fail("bench.py measures one GPU: this build has no multi-GPU path "
-             "(every box has one GPU); run with --gpus 1")
+        fail("bench.py measures one GPU: the library has no multi-GPU path; "
+             "run with --gpus 1")
     import torch
 
     if not torch.cuda.is_available():

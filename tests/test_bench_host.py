@@ -1,0 +1,106 @@
+"""Host-side parts of bench.py (CPU): the one-GPU guard, the rocprofv3
+summary (HBM byte counters scaled by a plain copy of known size, MFMA busy
+share) and the source-hash gate on stored traffic figures."""
+
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+DKV = "void treeattn::dkv_kernel<__bf16, 128>(treeattn::DkvArgs<__bf16, 128>)"
+FWD = "void treeattn::fwd_kernel<__bf16, 128, 12>(treeattn::FwdArgs<__bf16, 128>)"
+COPY = "__amd_rocclr_copyBuffer"
+
+
+def _write_csv(path, rows):
+    path.parent.mkdir(parents=True, exist_ok=True)
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=list(rows[0]))
+        w.writeheader()
+        w.writerows(rows)
+
+
+def _ctr(kernel, name, value):
+    return {"Kernel_Name": kernel, "Counter_Name": name, "Counter_Value": str(value)}
+
+
+@pytest.fixture
+def tmp_profiles(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "profiles" / "traffic.json"))
+    return tmp_path
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_byte_counters_are_scaled_by_the_copy(tmp_profiles):
+    # The 1 GiB copy reads as 524288 KiB fetched (half) and 1048576 KiB
+    # written (exact), so fetch counts are doubled and writes kept.
+    _write_csv(tmp_profiles / "f" / "run_counter_collection.csv", [
+        _ctr(COPY, "FETCH_SIZE", 524288), _ctr(DKV, "FETCH_SIZE", 1000),
+        _ctr(DKV, "FETCH_SIZE", 3000)])
+    _write_csv(tmp_profiles / "w" / "run_counter_collection.csv", [
+        _ctr(COPY, "WRITE_SIZE", 1048576), _ctr(DKV, "WRITE_SIZE", 10),
+        _ctr(DKV, "WRITE_SIZE", 30)])
+    text = bench.summarize([str(tmp_profiles / "f"), str(tmp_profiles / "w")], "the command")
+    assert "command: the command" in text
+    with open(bench.TRAFFIC_FILE) as f:
+        rec = json.load(f)
+    assert rec["calibration"] == {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
+    k = rec["kernels"]["dkv"]
+    assert k["read_bytes"] == [1000 * 1024 * 2, 3000 * 1024 * 2]
+    assert k["write_bytes"] == [10 * 1024, 30 * 1024]
+    # per launch: (reads + writes) / launches
+    assert k["hbm_bytes_per_launch"] == round((4000 * 2048 + 40 * 1024) / 2)
+    assert k["source_hash"] == bench.kernel_source_hash("dkv")
+    assert "fwd" not in rec["kernels"]
+
+
+def test_mfma_busy_share(tmp_profiles):
+    # GRBM_GUI_ACTIVE sums the 8 XCDs' active cycles; with 1024 SIMDs the
+    # matrix units could be busy for GRBM/8*1024 SIMD cycles.
+    _write_csv(tmp_profiles / "p" / "run_counter_collection.csv", [
+        _ctr(FWD, "GRBM_GUI_ACTIVE", 8 * 1000), _ctr(FWD, "SQ_VALU_MFMA_BUSY_CYCLES", 1024 * 250),
+        _ctr(DKV, "GRBM_GUI_ACTIVE", 8 * 400), _ctr(DKV, "SQ_VALU_MFMA_BUSY_CYCLES", 1024 * 300)])
+    text = bench.summarize([str(tmp_profiles / "p")], "c")
+    assert "fwd: 0.250" in text
+    assert "dkv: 0.750" in text
+    assert not os.path.exists(bench.TRAFFIC_FILE)
+
+
+def test_kernel_stats_table(tmp_profiles):
+    _write_csv(tmp_profiles / "k" / "run_kernel_stats.csv", [
+        {"Name": DKV, "Calls": "4", "AverageNs": "2500000", "TotalDurationNs": "10000000",
+         "Percentage": "60.0"},
+        {"Name": FWD, "Calls": "2", "AverageNs": "1000000", "TotalDurationNs": "2000000",
+         "Percentage": "12.0"}])
+    text = bench.summarize([str(tmp_profiles / "k")], "c")
+    lines = {l.split()[0]: l for l in text.splitlines() if l[:3] in ("dkv", "fwd")}
+    assert lines["dkv"].split()[1:4] == ["4", "2.500", "10.000"]
+    assert "(12 waves)" in lines["fwd"]
+
+
+def test_stored_traffic_needs_the_current_sources(tmp_profiles):
+    os.makedirs(bench.PROFILES)
+    rec = {"kernels": {"dkv": {"hbm_bytes_per_launch": 123,
+                               "source_hash": bench.kernel_source_hash("dkv")}}}
+    with open(bench.TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f)
+    assert bench.stored_traffic("dkv") == 123
+    assert bench.stored_traffic("fwd") is None
+    rec["kernels"]["dkv"]["source_hash"] = "0" * 16
+    with open(bench.TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f)
+    assert bench.stored_traffic("dkv") is None
