@@ -42,6 +42,8 @@
  * 4 GiB.  The packed head count is the largest power of two (at most 16)
  * dividing Hq / Hkv.  Larger problems are rejected with
  * TREE_ATTN_ERR_INVALID.
+ * Determinism.  No output is accumulated with atomics: every partial sum
+ * is added in a fixed order, so repeated calls give bit-identical results.
  * Errors.  0 on success, else a negative tree_attn_status.  Arguments are
  * checked on the host before any HIP call, so a rejected call enqueues
  * nothing and writes nothing.  TREE_ATTN_ERR_HIP reports a failed launch.
@@ -141,6 +143,9 @@ int tree_attn_prefill(const tree_attn_problem* problem, const void* q_p, const v
  *   in : k_p, v_p [sum P, Hkv, d] (prompt K/V state from prefill),
  *        q_r [sum r, Hq, d], k_r, v_r [sum r, Hkv, d]
  *   out: o_r [sum r, Hq, d], lse_r [Hq, sum r] (float32)
+ * With few response rows behind a long prompt, the prompt keys are cut into
+ * chunks processed in parallel; their float32 partial states go through
+ * the same merge as lse_merge() below.  The workspace size covers them.
  */
 int tree_attn_replay_fwd(const tree_attn_problem* problem, const void* k_p, const void* v_p,
                          const void* q_r, const void* k_r, const void* v_r, void* o_r,
