@@ -104,6 +104,17 @@ def test_edge_cases(name):
     compare(lib, ref, TOL[tree.dtype], label=name)
 
 
+@pytest.mark.parametrize("dtype,scale", [("bf16", 3.0), ("f32", 3.0)])
+def test_peaked_scores(dtype, scale):
+    """Inputs scaled up so that scores spread over tens of log2 units: the
+    running row maximum keeps growing from tile to tile, which drives the
+    forward's rescaling of O and the normaliser (taken only when a row's
+    maximum grows by more than 2^8)."""
+    tree = wl.Tree([700, 90], [[300, 129], [260]], 8, 2, 128 if dtype == "bf16" else 64, dtype)
+    _, _, lib, ref = _case(tree, 13, scale, f"peaked x{scale}")
+    compare(lib, ref, TOL[dtype], label=f"peaked {dtype}")
+
+
 def test_zero_prompt_upstream_gradient():
     """dO_P = 0: dQ_P must be exactly zero; everything else still matches."""
     tree = wl.Tree([500], [[200, 64]], 8, 2, 128, "bf16")
