@@ -28,8 +28,8 @@ namespace {
 
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
-int ceil_div(int a, int b) { return (a + b - 1) / b; }
-int pad_len(int n) { return ceil_div(n, kPad) * kPad; }
+long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
+long long pad_len(long long n) { return ceil_div(n, kPad) * kPad; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
@@ -97,6 +97,9 @@ int validate_problem(const tree_attn_problem* p, bool need_device, Shape& s) {
   s.tile_q = kTileQ / s.hp;
   s.p_tokens = p->prompt_cu_h[ng];
   s.r_tokens = p->resp_cu_h[nb];
+  // every index the kernels form must fit in int32
+  const long long lim = (1LL << 31) - 1;
+  if ((s.p_tokens + s.r_tokens) * (long long)s.hq > lim) return TREE_ATTN_ERR_INVALID;
   for (int g = 0; g < ng; ++g) {
     const int len = p->prompt_cu_h[g + 1] - p->prompt_cu_h[g];
     s.max_prompt = std::max(s.max_prompt, len);
@@ -136,8 +139,6 @@ int validate_problem(const tree_attn_problem* p, bool need_device, Shape& s) {
     s.k_items_replay += (long long)ceil_div(plen, kTileKV) * sg;
     if (sg > 1) s.part_rows += (long long)sg * plen;
   }
-  // every index the kernels form must fit in int32
-  const long long lim = (1LL << 31) - 1;
   if (s.p_pad * s.hp > lim || s.r_pad * s.hp > lim) return TREE_ATTN_ERR_INVALID;
   if (s.k_items_replay * s.hkv > lim || s.part_rows > lim)
     return TREE_ATTN_ERR_INVALID;
@@ -147,7 +148,6 @@ int validate_problem(const tree_attn_problem* p, bool need_device, Shape& s) {
     const long long by_len = s.max_prompt / kMinChunkKeys;
     s.col_splits = (int)std::max(1LL, std::min({by_fill, by_len, (long long)kMaxColSplits}));
   }
-  if ((s.p_tokens + s.r_tokens) * (long long)s.hq > lim) return TREE_ATTN_ERR_INVALID;
   // tile copies address a head group's slice of a transposed copy with a
   // 32-bit byte offset
   const long long slice = (long long)s.d * std::max(s.p_pad, s.r_pad) * s.hp * (long long)s.esz;

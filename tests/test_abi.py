@@ -73,6 +73,25 @@ def test_invalid_problem_rejected(kw, code):
     assert e.value.code == code
 
 
+@pytest.mark.parametrize("prompt,resp,heads", [
+    (2 ** 31 - 1, 0, 1),          # padding the prompt to 64 tokens passes int32
+    (2 ** 30, 2 ** 30, 1),        # prompt + response tokens reach 2^31
+    (2 ** 27, 0, 16),             # tokens x query heads reach 2^31
+])
+def test_token_totals_beyond_int32_rejected(prompt, resp, heads):
+    """Indices the kernels form must fit in int32; such problems are
+    rejected on the host, before any per-length arithmetic can overflow."""
+    kw = dict(prompt_cu=[0, prompt], num_q_heads=heads, num_kv_heads=1, head_dim=64)
+    if resp:
+        kw.update(group_branch_cu=[0, 1], resp_cu=[0, resp])
+    else:
+        kw.update(group_branch_cu=[0, 0], resp_cu=[0])
+    for op in range(4):
+        with pytest.raises(ops.TreeAttnError) as e:
+            ops.tree_attn_workspace_size(small_problem(**kw), op)
+        assert e.value.code == -1
+
+
 def test_transposed_copy_offset_limit():
     """A head group's slice of a transposed copy is addressed with 32-bit
     byte offsets: head_dim * padded tokens * packed heads * element size must
