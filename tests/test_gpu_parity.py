@@ -63,6 +63,10 @@ EDGE = {
     "empty branches": wl.Tree([200, 77], [[0, 65, 0], [0]], 4, 1, 128, "bf16"),
     "group without branches": wl.Tree([90, 150], [[], [40, 300]], 4, 4, 128, "bf16"),
     "empty prompt": wl.Tree([0, 64], [[31, 200], [7]], 4, 2, 128, "bf16"),
+    # no branch anywhere: replay is empty and the seeds are zero
+    "no branches at all": wl.Tree([100, 64], [[], []], 4, 2, 128, "bf16"),
+    # every prompt empty: replay is plain causal attention per branch
+    "all prompts empty": wl.Tree([0, 0], [[10, 70], [33]], 4, 2, 64, "bf16"),
     "MHA head_dim 64": wl.Tree([300], [[100, 257]], 3, 3, 64, "bf16"),
     "GQA 7:1 (Qwen2.5-7B grouping)": wl.Tree([260], [[90, 130]], 14, 2, 128, "bf16"),
     "MQA": wl.Tree([129], [[64, 65]], 8, 1, 128, "bf16"),
