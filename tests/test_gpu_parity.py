@@ -119,6 +119,34 @@ def test_peaked_scores(dtype, scale):
     compare(lib, ref, TOL[dtype], label=f"peaked {dtype}")
 
 
+def _random_tree(seed):
+    """A small random batch of trees: 1-3 groups, 0-6 branches each,
+    prompts of 0-300 tokens and branches of 0-260 (zero-length ones
+    included), a random GQA ratio, head_dim and dtype."""
+    rng = np.random.default_rng(seed)
+    hkv = int(rng.choice([1, 2, 3]))
+    hq = hkv * int(rng.choice([1, 2, 3, 4, 6, 8]))
+    d = int(rng.choice([64, 128]))
+    dtype = "f32" if rng.random() < 0.25 else "bf16"
+    ng = int(rng.integers(1, 4))
+    prompts = [0 if rng.random() < 0.15 else int(x) for x in rng.integers(1, 301, ng)]
+    branches = []
+    for _ in range(ng):
+        nb = int(rng.integers(0, 7))
+        lens = rng.integers(0, 261, nb)
+        lens[rng.random(nb) < 0.15] = 0
+        branches.append([int(x) for x in lens])
+    return wl.Tree(prompts, branches, hq, hkv, d, dtype)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_trees(seed):
+    tree = _random_tree(1000 + seed)
+    vs = 0.125 if tree.dtype == "f32" else 1.0
+    _, _, lib, ref = _case(tree, 50 + seed, vs, f"random {seed}")
+    compare(lib, ref, TOL[tree.dtype], label=f"random {seed}")
+
+
 def test_zero_prompt_upstream_gradient():
     """dO_P = 0: dQ_P must be exactly zero; everything else still matches."""
     tree = wl.Tree([500], [[200, 64]], 8, 2, 128, "bf16")
