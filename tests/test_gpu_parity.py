@@ -147,6 +147,32 @@ def test_random_trees(seed):
     compare(lib, ref, TOL[tree.dtype], label=f"random {seed}")
 
 
+def _random_split_tree(seed):
+    """Random trees that take the split paths: a long prompt (2048-4096
+    tokens) with a few short branches cuts the replay prompt column into
+    chunks; a short prompt (16-128) with many branches splits the prompt
+    key tiles over branch ranges."""
+    rng = np.random.default_rng(seed)
+    hkv = int(rng.choice([1, 2]))
+    hq = hkv * int(rng.choice([1, 2, 4]))
+    d = int(rng.choice([64, 128]))
+    if seed % 2 == 0:
+        prompts = [int(rng.integers(2048, 4097))]
+        branches = [[int(x) for x in rng.integers(1, 101, int(rng.integers(1, 4)))]]
+    else:
+        prompts = [int(x) for x in rng.integers(16, 129, int(rng.integers(1, 3)))]
+        branches = [[int(x) for x in rng.integers(64, 301, int(rng.integers(6, 13)))]
+                    for _ in prompts]
+    return wl.Tree(prompts, branches, hq, hkv, d, "bf16")
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_random_split_trees(seed):
+    tree = _random_split_tree(2000 + seed)
+    _, _, lib, ref = _case(tree, 70 + seed, 1.0, f"random split {seed}")
+    compare(lib, ref, TOL["bf16"], label=f"random split {seed}")
+
+
 def test_zero_prompt_upstream_gradient():
     """dO_P = 0: dQ_P must be exactly zero; everything else still matches."""
     tree = wl.Tree([500], [[200, 64]], 8, 2, 128, "bf16")
