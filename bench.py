@@ -65,13 +65,25 @@ def kernel_source_hash(kind):
     return h.hexdigest()[:16]
 
 
-def stored_traffic(kind):
+def profiled_workload(command):
+    """The workload a profiled bench.py command ran (its --workload, else the
+    default)."""
+    import re
+
+    m = re.search(r"--workload[ =](\S+)", command or "")
+    return m.group(1) if m else "prompt_heavy"
+
+
+def stored_traffic(kind, workload):
     """HBM bytes per launch measured by rocprofv3 for this kernel, if the
-    measurement was taken on the current sources; else None."""
+    measurement was taken on this workload and the current sources; else
+    None."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
+        return None
+    if rec.get("workload", profiled_workload(rec.get("command", ""))) != workload:
         return None
     k = rec.get("kernels", {}).get(kind)
     if not k or k.get("source_hash") != kernel_source_hash(kind):
@@ -203,7 +215,7 @@ def measure_workload(name, steps, warmup, flattened=True):
     rep["roofline"] = {
         "kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
         "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
-        "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": stored_traffic(dom),
+        "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": stored_traffic(dom, name),
         "flops_per_pair_per_dim": KERNEL_FLOPS_PER_PAIR_DIM[dom],
         "launches_per_step": 2, "ms_per_step": round(kern[dom], 4),
     }
@@ -367,7 +379,8 @@ def summarize(dirs, command):
         lines.append("HBM bytes per launch (KiB counter x 1024 x calibration), launches in order:")
         lines.append(f"calibration from a 1 GiB device copy: FETCH_SIZE x{calib['FETCH_SIZE']:.3f}, "
                      f"WRITE_SIZE x{calib['WRITE_SIZE']:.3f}")
-        rec = {"kernels": {}, "calibration": calib, "command": command}
+        rec = {"kernels": {}, "calibration": calib, "command": command,
+               "workload": profiled_workload(command)}
         for kind, d in traffic.items():
             f = d.get("FETCH_SIZE", [])
             w = d.get("WRITE_SIZE", [])

@@ -92,15 +92,33 @@ def test_kernel_stats_table(tmp_profiles):
     assert "(12 waves)" in lines["fwd"]
 
 
-def test_stored_traffic_needs_the_current_sources(tmp_profiles):
+def test_stored_traffic_needs_the_current_sources_and_workload(tmp_profiles):
     os.makedirs(bench.PROFILES)
     rec = {"kernels": {"dkv": {"hbm_bytes_per_launch": 123,
-                               "source_hash": bench.kernel_source_hash("dkv")}}}
+                               "source_hash": bench.kernel_source_hash("dkv")}},
+           "command": "python3 bench.py --steps 1"}
     with open(bench.TRAFFIC_FILE, "w") as f:
         json.dump(rec, f)
-    assert bench.stored_traffic("dkv") == 123
-    assert bench.stored_traffic("fwd") is None
+    assert bench.stored_traffic("dkv", "prompt_heavy") == 123
+    assert bench.stored_traffic("dkv", "response_heavy") is None
+    assert bench.stored_traffic("fwd", "prompt_heavy") is None
+    rec["command"] = "python3 bench.py --workload response_heavy"
+    with open(bench.TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f)
+    assert bench.stored_traffic("dkv", "response_heavy") == 123
+    assert bench.stored_traffic("dkv", "prompt_heavy") is None
     rec["kernels"]["dkv"]["source_hash"] = "0" * 16
     with open(bench.TRAFFIC_FILE, "w") as f:
         json.dump(rec, f)
-    assert bench.stored_traffic("dkv") is None
+    assert bench.stored_traffic("dkv", "response_heavy") is None
+
+
+def test_summary_records_the_profiled_workload(tmp_profiles):
+    _write_csv(tmp_profiles / "f" / "r_counter_collection.csv", [
+        _ctr(COPY, "FETCH_SIZE", 524288), _ctr(DKV, "FETCH_SIZE", 1000)])
+    _write_csv(tmp_profiles / "w" / "r_counter_collection.csv", [
+        _ctr(COPY, "WRITE_SIZE", 1048576), _ctr(DKV, "WRITE_SIZE", 10)])
+    bench.summarize([str(tmp_profiles / "f"), str(tmp_profiles / "w")],
+                    "rocprofv3 --pmc FETCH_SIZE -- python3 bench.py --workload long_mixed")
+    with open(bench.TRAFFIC_FILE) as f:
+        assert json.load(f)["workload"] == "long_mixed"
