@@ -44,7 +44,9 @@ KERNEL_FLOPS_PER_PAIR_DIM = {"fwd": 4, "dq": 6, "dkv": 8}
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PROFILES = os.path.join(ROOT, "profiles")
-TRAFFIC_FILE = os.path.join(PROFILES, "roofline_traffic.json")
+def traffic_file(workload):
+    """Where the HBM bytes per launch measured on a workload are stored."""
+    return os.path.join(PROFILES, f"roofline_traffic_{workload}.json")
 # Sources each main kernel is built from; a stored traffic figure is only
 # reported while these are unchanged.
 KERNEL_SOURCES = {
@@ -79,11 +81,11 @@ def stored_traffic(kind, workload):
     measurement was taken on this workload and the current sources; else
     None."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(workload)) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("workload", profiled_workload(rec.get("command", ""))) != workload:
+    if rec.get("workload") != workload:
         return None
     k = rec.get("kernels", {}).get(kind)
     if not k or k.get("source_hash") != kernel_source_hash(kind):
@@ -392,7 +394,7 @@ def summarize(dirs, command):
                                         "source_hash": kernel_source_hash(kind),
                                         "read_bytes": [round(x) for x in f],
                                         "write_bytes": [round(x) for x in w]}
-        with open(TRAFFIC_FILE, "w") as fh:
+        with open(traffic_file(rec["workload"]), "w") as fh:
             json.dump(rec, fh, indent=1)
     other = {c: v for c, v in counters.items() if c not in ("FETCH_SIZE", "WRITE_SIZE")}
     if other:

@@ -34,7 +34,6 @@ def _ctr(kernel, name, value):
 @pytest.fixture
 def tmp_profiles(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "profiles" / "traffic.json"))
     return tmp_path
 
 
@@ -56,7 +55,7 @@ def test_byte_counters_are_scaled_by_the_copy(tmp_profiles):
         _ctr(DKV, "WRITE_SIZE", 30)])
     text = bench.summarize([str(tmp_profiles / "f"), str(tmp_profiles / "w")], "the command")
     assert "command: the command" in text
-    with open(bench.TRAFFIC_FILE) as f:
+    with open(bench.traffic_file("prompt_heavy")) as f:
         rec = json.load(f)
     assert rec["calibration"] == {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
     k = rec["kernels"]["dkv"]
@@ -77,7 +76,7 @@ def test_mfma_busy_share(tmp_profiles):
     text = bench.summarize([str(tmp_profiles / "p")], "c")
     assert "fwd: 0.250" in text
     assert "dkv: 0.750" in text
-    assert not os.path.exists(bench.TRAFFIC_FILE)
+    assert not os.listdir(bench.PROFILES)
 
 
 def test_kernel_stats_table(tmp_profiles):
@@ -96,20 +95,20 @@ def test_stored_traffic_needs_the_current_sources_and_workload(tmp_profiles):
     os.makedirs(bench.PROFILES)
     rec = {"kernels": {"dkv": {"hbm_bytes_per_launch": 123,
                                "source_hash": bench.kernel_source_hash("dkv")}},
-           "command": "python3 bench.py --steps 1"}
-    with open(bench.TRAFFIC_FILE, "w") as f:
-        json.dump(rec, f)
-    assert bench.stored_traffic("dkv", "prompt_heavy") == 123
-    assert bench.stored_traffic("dkv", "response_heavy") is None
-    assert bench.stored_traffic("fwd", "prompt_heavy") is None
-    rec["command"] = "python3 bench.py --workload response_heavy"
-    with open(bench.TRAFFIC_FILE, "w") as f:
-        json.dump(rec, f)
+           "workload": "response_heavy"}
+
+    def store(r, name):
+        with open(bench.traffic_file(name), "w") as f:
+            json.dump(r, f)
+
+    store(rec, "response_heavy")
     assert bench.stored_traffic("dkv", "response_heavy") == 123
     assert bench.stored_traffic("dkv", "prompt_heavy") is None
+    assert bench.stored_traffic("fwd", "response_heavy") is None
+    store(rec, "prompt_heavy")  # a record under the wrong name is ignored
+    assert bench.stored_traffic("dkv", "prompt_heavy") is None
     rec["kernels"]["dkv"]["source_hash"] = "0" * 16
-    with open(bench.TRAFFIC_FILE, "w") as f:
-        json.dump(rec, f)
+    store(rec, "response_heavy")
     assert bench.stored_traffic("dkv", "response_heavy") is None
 
 
@@ -120,5 +119,5 @@ def test_summary_records_the_profiled_workload(tmp_profiles):
         _ctr(COPY, "WRITE_SIZE", 1048576), _ctr(DKV, "WRITE_SIZE", 10)])
     bench.summarize([str(tmp_profiles / "f"), str(tmp_profiles / "w")],
                     "rocprofv3 --pmc FETCH_SIZE -- python3 bench.py --workload long_mixed")
-    with open(bench.TRAFFIC_FILE) as f:
+    with open(bench.traffic_file("long_mixed")) as f:
         assert json.load(f)["workload"] == "long_mixed"
