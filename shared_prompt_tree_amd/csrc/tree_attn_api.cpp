@@ -48,6 +48,9 @@ struct Shape {
   long long part_rows = 0;     // partial-seed rows of the split groups
   int max_prompt = 0;          // longest prompt
   int col_splits = 1;          // prompt-column chunks of the replay query lists
+  long long own_work = 0;      // own-branch 64-key steps over the replay query tiles
+  long long own_max = 0;       // most own-branch steps of one query tile
+  long long prompt_work = 0;   // prompt-column 64-key steps over the replay query tiles
 };
 
 // Key-stationary workgroups one launch should have in flight on the whole
@@ -55,12 +58,52 @@ struct Shape {
 // than the launch's total rows divided by this is worth splitting.
 constexpr long long kSplitSlots = 512;
 
-// Replay query-stationary launches (forward, dQ) with fewer workgroups than
-// this cut each prompt column into chunks (each at least kMinChunkKeys keys)
-// until they have about this many; the chunks' partial results are merged.
-constexpr long long kColFill = 512;
+// Replay query-stationary launches (forward, dQ) may cut each prompt column
+// into S chunks of whole 64-key tiles (each at least kMinChunkKeys keys);
+// the chunks' partial results are merged afterwards.  S is chosen by a
+// makespan model, in units of one 64-key step of one workgroup:
+//   items      q_wgs * S, each costing its prompt chunk, its own-branch
+//              tiles (last chunk only) and kItemOverhead;
+//   makespan   max(rounds * mean item, longest item), rounds =
+//              ceil(items / kQSlots) (one 8-wave workgroup per CU);
+//   merge      2 * S * response rows * Hq * d * 4 bytes of float32 partials
+//              written and read back, at kMergeBytesPerUnit per unit
+//              (HBM at ~5 TB/s against ~2 us per unit).
+// Only launches of up to kColSearchWgs workgroups are considered: beyond
+// that a partial last round costs little.
 constexpr int kMinChunkKeys = 1024;
 constexpr int kMaxColSplits = 64;
+constexpr long long kQSlots = 256;
+constexpr long long kColSearchWgs = 8 * kQSlots;
+constexpr double kItemOverhead = 1.0;
+constexpr double kMergeBytesPerUnit = 1e7;
+
+// Prompt-column chunks S of the replay query lists (see the model above).
+int choose_col_splits(const Shape& s) {
+  const long long n_hg = s.hq / s.hp;
+  const long long q_wgs = s.q_items_replay * n_hg;
+  const long long smax =
+      std::min<long long>(kMaxColSplits, s.max_prompt / kMinChunkKeys);
+  if (q_wgs == 0 || q_wgs > kColSearchWgs || smax < 2) return 1;
+  const double prompt = (double)s.prompt_work * n_hg, own = (double)s.own_work * n_hg;
+  const long long ptiles_max = ceil_div(s.max_prompt, kTileK);
+  const double row_bytes = (double)s.r_tokens * s.hq * s.d * 4;
+  int best = 1;
+  double best_t = 0;
+  for (long long S = 1; S <= smax; ++S) {
+    const long long items = q_wgs * S;
+    const double work = prompt + own + kItemOverhead * items;
+    const double longest = (double)ceil_div(ptiles_max, S) + s.own_max + kItemOverhead;
+    const double rounds = (double)ceil_div(items, kQSlots);
+    double t = std::max(rounds * work / items, longest);
+    if (S > 1) t += 2.0 * S * row_bytes / kMergeBytesPerUnit;
+    if (S == 1 || t < best_t) {
+      best = (int)S;
+      best_t = t;
+    }
+  }
+  return best;
+}
 
 int validate_problem(const tree_attn_problem* p, bool need_device, Shape& s) {
   if (!p) return TREE_ATTN_ERR_INVALID;
@@ -116,6 +159,11 @@ int validate_problem(const tree_attn_problem* p, bool need_device, Shape& s) {
     const int len = p->resp_cu_h[i + 1] - p->resp_cu_h[i];
     s.r_pad += pad_len(len);
     s.q_items_replay += ceil_div(len, s.tile_q);
+    for (long long q = s.tile_q; q < len + s.tile_q; q += s.tile_q) {  // own keys per query tile
+      const long long own = ceil_div(std::min<long long>(q, len), kTileK);
+      s.own_work += own;
+      s.own_max = std::max(s.own_max, own);
+    }
     s.wq_items_replay += ceil_div(len, kTileQWide / s.hp);
     const long long n = ceil_div(len, kTileKV);
     s.k_items_replay += n;
@@ -127,6 +175,9 @@ int validate_problem(const tree_attn_problem* p, bool need_device, Shape& s) {
     const long long rows =
         (long long)p->resp_cu_h[p->group_branch_cu_h[g + 1]] - p->resp_cu_h[p->group_branch_cu_h[g]];
     total += (long long)ceil_div(plen, kTileKV) * rows;
+    for (int i = p->group_branch_cu_h[g]; i < p->group_branch_cu_h[g + 1]; ++i)
+      s.prompt_work += ceil_div(p->resp_cu_h[i + 1] - p->resp_cu_h[i], s.tile_q) *
+                       ceil_div(plen, kTileK);
   }
   s.split_target = std::max(longest, (total * s.hkv + kSplitSlots - 1) / kSplitSlots);
   for (int g = 0; g < ng; ++g) {
@@ -142,12 +193,7 @@ int validate_problem(const tree_attn_problem* p, bool need_device, Shape& s) {
   if (s.p_pad * s.hp > lim || s.r_pad * s.hp > lim) return TREE_ATTN_ERR_INVALID;
   if (s.k_items_replay * s.hkv > lim || s.part_rows > lim)
     return TREE_ATTN_ERR_INVALID;
-  const long long q_wgs = s.q_items_replay * (s.hq / s.hp);
-  if (q_wgs > 0 && q_wgs < kColFill) {
-    const long long by_fill = (kColFill + q_wgs - 1) / q_wgs;
-    const long long by_len = s.max_prompt / kMinChunkKeys;
-    s.col_splits = (int)std::max(1LL, std::min({by_fill, by_len, (long long)kMaxColSplits}));
-  }
+  s.col_splits = choose_col_splits(s);
   // tile copies address a head group's slice of a transposed copy with a
   // 32-bit byte offset
   const long long slice = (long long)s.d * std::max(s.p_pad, s.r_pad) * s.hp * (long long)s.esz;

@@ -125,9 +125,10 @@ def test_replay_workspace_holds_split_partial_seeds():
 
 def test_replay_workspace_holds_prompt_column_partials():
     """Few response rows behind a long prompt: 4 query workgroups (8 heads
-    packed 4 per kv head, 2 branches of one tile) -> the prompt column is cut
-    into min(ceil(512 / 4), 8192 // 1024) = 8 chunks, whose float32 partial
-    O (and LSE) the replay-forward workspace holds."""
+    packed 4 per kv head, 2 branches of one tile) fit one round however the
+    128-tile prompt column is cut, so the longest item decides and the
+    column is cut into the most chunks of >= 1024 keys, 8192 // 1024 = 8;
+    the replay-forward workspace holds their float32 partial O (and LSE)."""
     kw = dict(prompt_cu=[0, 8192], group_branch_cu=[0, 2], resp_cu=[0, 40, 73],
               num_q_heads=8, num_kv_heads=2, head_dim=128)
     split = ops.tree_attn_workspace_size(small_problem(**kw), ops.OP_REPLAY_FWD)
@@ -135,6 +136,32 @@ def test_replay_workspace_holds_prompt_column_partials():
     whole = ops.tree_attn_workspace_size(small_problem(**kw), ops.OP_REPLAY_FWD)
     partial = 8 * 73 * 8 * 128 * 4 + 8 * 8 * 73 * 4
     assert split - whole >= partial
+
+
+def _column_chunks(prompt, branches, hq=32, hkv=8, d=128):
+    """Prompt-column chunks of a replay forward, read off its workspace: the
+    float32 partial O and LSE that only a split launch holds."""
+    def ws(p_len):
+        kw = dict(prompt_cu=[0, p_len], group_branch_cu=[0, len(branches)],
+                  resp_cu=np.concatenate([[0], np.cumsum(branches)]).tolist(),
+                  num_q_heads=hq, num_kv_heads=hkv, head_dim=d)
+        return ops.tree_attn_workspace_size(small_problem(**kw), ops.OP_REPLAY_FWD)
+    vt = lambda p_len: hkv * d * (-(-p_len // 64) * 64) * 2  # V^T copy of the prompt
+    r = int(np.sum(branches))
+    extra = ws(prompt) - ws(1000) - (vt(prompt) - vt(1000))  # 1000 keys cannot be cut
+    return extra / (r * hq * d * 4 + hq * r * 4)
+
+
+def test_column_split_model():
+    """The prompt-column split follows the makespan model: 512 workgroups
+    (8 branches of 512 tokens, 32/8 heads) fill exactly two rounds of the
+    256 CUs and are not cut; 520 (13 branches of 260) would need a third,
+    nearly empty round, so the column is cut (into 6 chunks); a few rows
+    behind a 131072-token prompt are cut until the items fit one round."""
+    assert _column_chunks(32768, [512] * 8) == pytest.approx(0, abs=0.05)
+    assert _column_chunks(32768, [260] * 13) == pytest.approx(6, abs=0.05)
+    assert _column_chunks(131072, [64] * 8) == pytest.approx(4, abs=0.05)
+    assert _column_chunks(2048, [150] * 11) == pytest.approx(2, abs=0.05)
 
 
 def test_bad_op_and_null_out_pointer():

@@ -88,10 +88,14 @@ EDGE = {
                                    "bf16"),
     "split f32": wl.Tree([64], [[64] * 5], 2, 1, 64, "f32"),
     # Few response rows behind a long prompt: the replay query lists cut the
-    # prompt column into chunks until the launch has ~512 workgroups, each
-    # chunk >= 1024 keys; forward partials merged by lse_merge, dQ partials
-    # summed.  4 workgroups -> 8 chunks of 1024 keys here.
+    # prompt column into chunks of >= 1024 keys, as many as a makespan model
+    # finds worth their merge; forward partials merged by lse_merge, dQ
+    # partials summed.  4 workgroups -> 8 chunks of 1024 keys here.
     "split prompt column": wl.Tree([8192], [[40, 33]], 8, 2, 128, "bf16"),
+    # 264 workgroups: one more than a full round of 256 CUs, so the model
+    # cuts the 2048-key prompt into 2 chunks (3 rounds of half-length items
+    # instead of 2 rounds of whole ones).
+    "split prompt column past a full round": wl.Tree([2048], [[150] * 11], 32, 8, 128, "bf16"),
     # 6 workgroups -> 4 chunks; prompts of 47 and 79 tiles, an empty branch.
     "split prompt column, two groups": wl.Tree([3000, 5000], [[17, 0, 64], [100]], 4, 2, 64,
                                                "bf16"),
