@@ -53,9 +53,10 @@ struct Shape {
   long long prompt_work = 0;   // prompt-column 64-key steps over the replay query tiles
 };
 
-// Key-stationary workgroups one launch should have in flight on the whole
-// GPU (two per compute unit of a 256-CU MI355X): a work item reading more
-// than the launch's total rows divided by this is worth splitting.
+// A replay key-stationary item reading more than the launch's total rows
+// divided by this is worth splitting: with one dK/dV workgroup per compute
+// unit of a 256-CU MI355X, no item then exceeds half of one CU's fair share,
+// so the largest-first order can balance the launch.
 constexpr long long kSplitSlots = 512;
 
 // Replay query-stationary launches (forward, dQ) may cut each prompt column
