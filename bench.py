@@ -16,12 +16,14 @@ Prints one JSON line.  Besides the headline numbers it carries:
   breakdown_ms       time per entry point (HIP events between the calls)
   roofline           the dominant kernel's own duration (HIP events recorded
                      by the library around that kernel) against the bf16
-                     MFMA peak
+                     MFMA peak; per launch, its measured HBM bytes, the
+                     algorithmic bytes and the achieved HBM bandwidth
   flattened_baseline the same attention computed the way flattened context
                      parallelism does it: every (prompt, response) pair as
                      its own causal sequence, with the same kernels
   cpu_baseline       the float64 oracle on a bounded sample, host cores
-  also               the same measurement for a second workload
+  also               the same measurement for further workloads (response-heavy
+                     and long-mixed by default; long-mixed with 3 timed steps)
 """
 
 from __future__ import annotations
@@ -93,14 +95,102 @@ def stored_traffic(kind, workload):
     return k.get("hbm_bytes_per_launch")
 
 
+def stored_launch_traffic(kind, workload):
+    """Measured HBM (read, write) bytes of each launch of a main kernel in one
+    step, in call order, from the stored profile of this workload and the
+    current sources; None when there is none.  The profiled run times one
+    step twice, so its launches repeat the step's sequence."""
+    try:
+        with open(traffic_file(workload)) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    k = rec.get("kernels", {}).get(kind)
+    if rec.get("workload") != workload or not k or k.get("source_hash") != kernel_source_hash(kind):
+        return None
+    r, w = k.get("read_bytes", []), k.get("write_bytes", [])
+    if len(r) < 2 or len(r) != len(w):
+        return None
+    # launches c = 0, 1 of every step, averaged over the profiled steps
+    return [(sum(r[c::2]) / len(r[c::2]), sum(w[c::2]) / len(w[c::2])) for c in range(2)]
+
+
+# Which entry point issues launch c (0, 1) of a main kernel in one step.
+LAUNCH_CALLS = {"fwd": ("prefill", "replay_fwd"), "dq": ("replay_bwd", "prefill_bwd"),
+                "dkv": ("replay_bwd", "prefill_bwd")}
+
+
+def algorithmic_bytes(tree, kind, call):
+    """Least HBM traffic of one launch: every operand read once and every
+    result written once (the pre-transposed copies and work lists the
+    kernels also read are not counted).
+      fwd prefill     Q, K, V in; O, LSE out (prompt)
+      fwd replay      Q_R, K_R, V_R, K_P, V_P in; O_R, LSE_R out
+      dq              Q, dO, LSE, D of the query rows and the K, V they read
+                      in; dQ out
+      dkv replay_bwd  Q_R, dO_R, LSE_R, D_R and K, V of prompt and responses
+                      in; dK_R, dV_R (I/O dtype) and the float32 prompt seeds
+                      out
+      dkv prefill_bwd Q_P, dO_P, LSE_P, D_P, K_P, V_P and the float32 seeds
+                      in; dK_P, dV_P out"""
+    esz = 4 if tree.dtype == "f32" else 2
+    hq, hkv, d = tree.hq, tree.hkv, tree.d
+    tp, tr = tree.prompt_tokens, tree.resp_tokens
+    q_rows = lambda n: n * hq * d * esz       # Q, O, dO or dQ of n tokens
+    kv_rows = lambda n: n * hkv * d * esz     # K, V, dK or dV of n tokens
+    seeds = tp * hkv * d * 4
+    rows = tp if call in ("prefill", "prefill_bwd") else tr
+    if kind == "fwd":
+        keys = tp if call == "prefill" else tp + tr
+        return q_rows(rows) + 2 * kv_rows(keys) + q_rows(rows) + rows * hq * 4
+    if kind == "dq":
+        keys = tp if call == "prefill_bwd" else tp + tr
+        return 2 * q_rows(rows) + 2 * rows * hq * 4 + 2 * kv_rows(keys) + q_rows(rows)
+    if call == "replay_bwd":
+        return (2 * q_rows(tr) + 2 * tr * hq * 4 + 2 * kv_rows(tp + tr) + 2 * kv_rows(tr)
+                + 2 * seeds)
+    return 2 * q_rows(tp) + 2 * tp * hq * 4 + 2 * kv_rows(tp) + 2 * seeds + 2 * kv_rows(tp)
+
+
+def launch_report(tree, kind, ms, stored):
+    """Per launch of the dominant kernel in one step: its own duration and
+    FLOP rate, its measured HBM bytes (rocprofv3 counters of the stored
+    profile, null without one), the algorithmic bytes and the achieved HBM
+    bandwidth."""
+    from shared_prompt_tree_amd import workloads as wl
+
+    pc = wl.pair_counts(tree)
+    pairs = {"prefill": pc["prefill"], "prefill_bwd": pc["prefill"],
+             "replay_fwd": pc["replay_prompt"] + pc["replay_own"],
+             "replay_bwd": pc["replay_prompt"] + pc["replay_own"]}
+    out = []
+    for c, call in enumerate(LAUNCH_CALLS[kind]):
+        flops = pairs[call] * tree.hq * tree.d * KERNEL_FLOPS_PER_PAIR_DIM[kind]
+        alg = algorithmic_bytes(tree, kind, call)
+        rec = {"call": call, "ms": round(ms[c], 4),
+               "tflops": round(flops / (ms[c] * 1e-3) / 1e12, 2) if ms[c] > 0 else None,
+               "algorithmic_bytes": int(alg), "hbm_bytes": None, "hbm_gbps": None,
+               "hbm_over_algorithmic": None}
+        if stored is not None:
+            hbm = stored[c][0] + stored[c][1]
+            rec["hbm_bytes"] = int(round(hbm))
+            rec["hbm_read_bytes"] = int(round(stored[c][0]))
+            rec["hbm_gbps"] = round(hbm / (ms[c] * 1e-3) / 1e9, 1) if ms[c] > 0 else None
+            rec["hbm_over_algorithmic"] = round(hbm / alg, 2) if alg > 0 else None
+        out.append(rec)
+    return out
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="prompt_heavy")
-    p.add_argument("--also", default="response_heavy",
-                   help="second workload measured the same way ('none' to skip)")
+    p.add_argument("--also", default="response_heavy,long_mixed",
+                   help="comma-separated further workloads measured the same way "
+                        "('none' to skip); each is timed with at most ALSO_STEPS[name] "
+                        "steps and ALSO_WARMUP[name] warmup steps")
     p.add_argument("--no-flattened", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-workers", type=int, default=0)
@@ -115,12 +205,18 @@ def parse():
     return p.parse_args()
 
 
+# Further workloads whose step takes over a second are timed with fewer
+# steps, so the default run stays within a few minutes.
+ALSO_STEPS = {"long_mixed": 3}
+ALSO_WARMUP = {"long_mixed": 1}
+
+
 def fail(msg):
     print(msg, file=sys.stderr, flush=True)
     sys.exit(2)
 
 
-def measure_workload(name, steps, warmup, flattened=True):
+def measure_workload(name, steps, warmup, flattened=True, fms_hint=None):
     import torch
 
     from shared_prompt_tree_amd import ops
@@ -165,6 +261,7 @@ def measure_workload(name, steps, warmup, flattened=True):
         return e
 
     per_step = []
+    kern_launch = {(k, c): 0.0 for k in kern for c in range(2)}
     for _ in range(steps):
         evs = [new_event() for _ in range(5)]
         # kernel events: fwd in prefill and replay_fwd, dq and dkv in both bwd calls
@@ -196,6 +293,7 @@ def measure_workload(name, steps, warmup, flattened=True):
             part[n] += evs[i].elapsed_time(evs[i + 1]) / steps
         for (k, c), (a, b) in kev.items():
             kern[k] += a.elapsed_time(b) / steps
+            kern_launch[(k, c)] += a.elapsed_time(b) / steps
 
     pairs = wl.pair_counts(tree)
     useful = wl.useful_flops(tree)
@@ -214,12 +312,15 @@ def measure_workload(name, steps, warmup, flattened=True):
     kflops = {k: pairs["tree"] * hq * d * f for k, f in KERNEL_FLOPS_PER_PAIR_DIM.items()}
     dom = max(kern, key=kern.get)
     achieved = kflops[dom] / (kern[dom] * 1e-3) / 1e12
+    stored = stored_launch_traffic(dom, name)
     rep["roofline"] = {
         "kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
         "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
-        "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": stored_traffic(dom, name),
+        "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "traffic": None if stored is None else round(sum(r + w for r, w in stored) / len(stored)),
         "flops_per_pair_per_dim": KERNEL_FLOPS_PER_PAIR_DIM[dom],
         "launches_per_step": 2, "ms_per_step": round(kern[dom], 4),
+        "launches": launch_report(tree, dom, [kern_launch[(dom, c)] for c in range(2)], stored),
     }
     rep["kernel_tflops"] = {k: round(kflops[k] / (kern[k] * 1e-3) / 1e12, 2) for k in kern}
     # forward (prefill + replay_fwd) and backward (replay_bwd + prefill_bwd)
@@ -246,7 +347,7 @@ def measure_workload(name, steps, warmup, flattened=True):
 
         fstep()
         torch.cuda.synchronize()
-        fsteps = max(1, min(steps, 5))
+        fsteps = max(1, min(steps, 5 if fms_hint is None else fms_hint))
         ev0.record()
         for _ in range(fsteps):
             fstep()
@@ -452,22 +553,28 @@ def main():
     main_rep.pop("_tree")
     main_rep.pop("_tensors")
     torch.cuda.empty_cache()
-    also = None
-    if args.also and args.also != "none" and args.also != args.workload:
-        print(f"[bench] workload {args.also}", file=sys.stderr, flush=True)
-        a = measure_workload(args.also, args.steps, args.warmup, not args.no_flattened)
+    also = []
+    names = [] if args.also in ("", "none") else args.also.split(",")
+    for aname in [n for n in names if n != args.workload]:
+        a_steps = min(args.steps, ALSO_STEPS.get(aname, args.steps))
+        a_warm = min(args.warmup, ALSO_WARMUP.get(aname, args.warmup))
+        print(f"[bench] workload {aname}: warmup {a_warm}, steps {a_steps}", file=sys.stderr,
+              flush=True)
+        a = measure_workload(aname, a_steps, a_warm, not args.no_flattened,
+                             fms_hint=1 if aname in ALSO_STEPS else None)
         a.pop("_tree")
         a.pop("_tensors")
-        also = {
-            "workload": args.also, "value": round(a["tflops"], 2), "unit": "TFLOP/s",
+        also.append({
+            "workload": aname, "value": round(a["tflops"], 2), "unit": "TFLOP/s",
+            "steps": a_steps, "warmup": a_warm,
             "ms_per_step": round(a["ms_per_step"], 3), "step_ms_median": a["step_ms_median"],
             "pct_of_bf16_peak": round(100 * a["tflops"] / PEAK_BF16_TFLOPS, 2),
             "breakdown_ms": a["breakdown_ms"], "kernel_ms": a["kernel_ms"],
             "kernel_tflops": a["kernel_tflops"], "roofline": a["roofline"],
             "phases": a["phases"], "useful_tflops_12d": a["useful_tflops_12d"],
             "flattened_baseline": a.get("flattened_baseline"), "config": a["config"],
-        }
-        print(f"[bench] {args.also}: {a['ms_per_step']:.2f} ms/step, {a['tflops']:.1f} TFLOP/s",
+        })
+        print(f"[bench] {aname}: {a['ms_per_step']:.2f} ms/step, {a['tflops']:.1f} TFLOP/s",
               file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
     if args.copy_calibration_mib > 0:
@@ -506,7 +613,7 @@ def main():
         "roofline": main_rep["roofline"],
         "flattened_baseline": main_rep.get("flattened_baseline"),
         "cpu_baseline": cpu,
-        "also": also,
+        "also": also or None,
     }
     print(json.dumps(line), flush=True)
 

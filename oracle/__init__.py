@@ -6,6 +6,7 @@ with it.
 """
 
 from .tree_attention import (  # noqa: F401
+    causal_key_grads,
     causal_unit,
     lse_merge,
     tree_attention,

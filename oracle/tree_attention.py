@@ -46,6 +46,7 @@ import os
 import numpy as np
 
 __all__ = [
+    "causal_key_grads",
     "causal_unit",
     "lse_merge",
     "tree_attention",
@@ -102,6 +103,52 @@ def causal_unit(xq, xk, xv, do, scale, rows=None, chunk=512):
         dk[:kmax] += scale * (ds.T @ xq[r])
         dv[:kmax] += p.T @ g
     return o, lse, dq, dk, dv
+
+
+def causal_key_grads(xq, xk, xv, do, scale, rows, keys, chunk=256):
+    """Gradient of sum(dO * O) with respect to chosen keys and values of one
+    flattened causal sequence, from chosen query rows.
+
+    The definitions are those of ``causal_unit``: row t sees keys 0..t
+    (diagonal included), P = softmax(scale * Q K^T) over that whole range,
+    O = P V, D = rowsum(dO * O), dS = P * (dO V^T - D).  Only the columns in
+    ``keys`` of dP and dS are formed:
+        dK[j] = scale * sum_{t in rows} dS[t, j] q_t,
+        dV[j] = sum_{t in rows} P[t, j] dO_t.
+    Each chunk of rows still evaluates every row's softmax over its whole key
+    range (the normaliser and D need all of it); there is no online softmax.
+
+    xq, xk, xv, do: float64 [L, d]; rows: sorted query rows; keys: key
+    indices.  Returns (dk [len(keys), d], dv [len(keys), d]), sums over
+    ``rows`` only (the full gradient of key j when rows holds every t >= j).
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    keys = np.asarray(keys, dtype=np.int64)
+    d = xq.shape[1]
+    dk = np.zeros((len(keys), d))
+    dv = np.zeros((len(keys), d))
+    for a in range(0, len(rows), chunk):
+        r = rows[a:a + chunk]
+        kmax = int(r[-1]) + 1
+        s = xq[r] @ xk[:kmax].T
+        s *= scale
+        # keys after a row are hidden; only columns past the chunk's first
+        # row can be
+        tail = s[:, int(r[0]) + 1:]
+        tail[np.arange(int(r[0]) + 1, kmax)[None, :] > r[:, None]] = -np.inf
+        m = s.max(axis=1, keepdims=True)
+        s -= m
+        np.exp(s, out=s)
+        s /= s.sum(axis=1, keepdims=True)  # s now holds P
+        g = do[r]
+        dd = (g * (s @ xv[:kmax])).sum(axis=1, keepdims=True)  # D = rowsum(dO * O)
+        seen = keys < kmax
+        pk = np.zeros((len(r), len(keys)))
+        pk[:, seen] = s[:, keys[seen]]
+        dsk = pk * (g @ xv[keys].T - dd)
+        dk += scale * (dsk.T @ xq[r])
+        dv += pk.T @ g
+    return dk, dv
 
 
 def _as64(x):

@@ -1,6 +1,7 @@
 // Auxiliary kernels: the device-side work lists, transposed copies, the
 // backward row dot product, and the standalone partial-state merge.
 #include "device_common.h"
+#include "grid_math.h"
 #include "launch.h"
 
 namespace treeattn {
@@ -264,31 +265,32 @@ hipError_t launch_meta(const MetaArgs& a, hipStream_t s) {
 //
 // Prompt seeds of split groups: the splits' partial sums added in split
 // order (deterministic).  One thread per 4 floats of a prompt token.
-__global__ __launch_bounds__(256) void seed_reduce_kernel(SeedReduceArgs a) {
+__global__ __launch_bounds__(kAuxThreads) void seed_reduce_kernel(SeedReduceArgs a) {
   const int per_tok = a.width / 4;
-  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (long long)a.tokens * per_tok) return;
-  const int t = (int)(idx / per_tok), c = (int)(idx % per_tok) * 4;
-  int lo = 0, hi = a.n_groups - 1;  // group of token t: last g with prompt_cu[g] <= t
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (a.prompt_cu[mid] <= t) lo = mid;
-    else hi = mid - 1;
+  const long long n = (long long)a.tokens * per_tok;
+  for (long long idx = aux_first(blockIdx.x, threadIdx.x); idx < n; idx += aux_stride(gridDim.x)) {
+    const int t = (int)(idx / per_tok), c = (int)(idx % per_tok) * 4;
+    int lo = 0, hi = a.n_groups - 1;  // group of token t: last g with prompt_cu[g] <= t
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.prompt_cu[mid] <= t) lo = mid;
+      else hi = mid - 1;
+    }
+    const int g = lo;
+    const int sg = a.split_cu[g + 1] - a.split_cu[g];
+    if (sg <= 1) continue;
+    const int plen = a.prompt_cu[g + 1] - a.prompt_cu[g];
+    const size_t r0 = (size_t)a.part_row[g] + (t - a.prompt_cu[g]);
+    f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < sg; ++k) {
+      const size_t o = (r0 + (size_t)k * plen) * a.width + c;
+      sk += *reinterpret_cast<const f32x4*>(a.part_k + o);
+      sv += *reinterpret_cast<const f32x4*>(a.part_v + o);
+    }
+    const size_t o = (size_t)t * a.width + c;
+    *reinterpret_cast<f32x4*>(a.dk_seed + o) = sk;
+    *reinterpret_cast<f32x4*>(a.dv_seed + o) = sv;
   }
-  const int g = lo;
-  const int sg = a.split_cu[g + 1] - a.split_cu[g];
-  if (sg <= 1) return;
-  const int plen = a.prompt_cu[g + 1] - a.prompt_cu[g];
-  const size_t r0 = (size_t)a.part_row[g] + (t - a.prompt_cu[g]);
-  f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k < sg; ++k) {
-    const size_t o = (r0 + (size_t)k * plen) * a.width + c;
-    sk += *reinterpret_cast<const f32x4*>(a.part_k + o);
-    sv += *reinterpret_cast<const f32x4*>(a.part_v + o);
-  }
-  const size_t o = (size_t)t * a.width + c;
-  *reinterpret_cast<f32x4*>(a.dk_seed + o) = sk;
-  *reinterpret_cast<f32x4*>(a.dv_seed + o) = sv;
 }
 
 // ------------------------------------------------------------ chunk sums
@@ -297,26 +299,26 @@ __global__ __launch_bounds__(256) void seed_reduce_kernel(SeedReduceArgs a) {
 // order (deterministic), written in the output dtype.  One thread per 4
 // elements.
 template <typename T>
-__global__ __launch_bounds__(256) void sum_parts_kernel(const float* in, int parts, long long n,
-                                                        T* out) {
-  const long long i = ((long long)blockIdx.x * blockDim.x + threadIdx.x) * 4;
-  if (i >= n) return;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k < parts; ++k) acc += *reinterpret_cast<const f32x4*>(in + k * n + i);
+__global__ __launch_bounds__(kAuxThreads) void sum_parts_kernel(const float* in, int parts,
+                                                                long long n, T* out) {
+  for (long long q = aux_first(blockIdx.x, threadIdx.x); q < n / 4; q += aux_stride(gridDim.x)) {
+    const long long i = q * 4;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < parts; ++k) acc += *reinterpret_cast<const f32x4*>(in + k * n + i);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) out[i + e] = static_cast<T>(acc[e]);
+    for (int e = 0; e < 4; ++e) out[i + e] = static_cast<T>(acc[e]);
+  }
 }
 
 hipError_t launch_sum_parts(const float* in, int parts, long long n, void* out, int dtype,
                             hipStream_t s) {
   if (n == 0) return hipSuccess;
-  const long long threads = n / 4;
-  const int grid = (int)((threads + 255) / 256);
+  const int grid = (int)aux_blocks(n / 4);
   if (dtype == 1)
-    hipLaunchKernelGGL(sum_parts_kernel<bf16>, dim3(grid), dim3(256), 0, s, in, parts, n,
+    hipLaunchKernelGGL(sum_parts_kernel<bf16>, dim3(grid), dim3(kAuxThreads), 0, s, in, parts, n,
                        static_cast<bf16*>(out));
   else
-    hipLaunchKernelGGL(sum_parts_kernel<float>, dim3(grid), dim3(256), 0, s, in, parts, n,
+    hipLaunchKernelGGL(sum_parts_kernel<float>, dim3(grid), dim3(kAuxThreads), 0, s, in, parts, n,
                        static_cast<float*>(out));
   return hipGetLastError();
 }
@@ -324,8 +326,7 @@ hipError_t launch_sum_parts(const float* in, int parts, long long n, void* out, 
 hipError_t launch_seed_reduce(const SeedReduceArgs& a, hipStream_t s) {
   const long long n = (long long)a.tokens * (a.width / 4);
   if (n == 0) return hipSuccess;
-  const int grid = (int)((n + 255) / 256);
-  hipLaunchKernelGGL(seed_reduce_kernel, dim3(grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(seed_reduce_kernel, dim3((int)aux_blocks(n)), dim3(kAuxThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -336,61 +337,68 @@ hipError_t launch_seed_reduce(const SeedReduceArgs& a, hipStream_t s) {
 // hg*hp + col % hp; padding columns are written as zeros.
 
 template <typename T>
-__global__ __launch_bounds__(256) void transpose_kernel(TransposeArgs a) {
+__global__ __launch_bounds__(kAuxThreads) void transpose_kernel(TransposeArgs a) {
   constexpr int C = 64;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   T* tile = reinterpret_cast<T*>(smem_raw);  // [C][d + 8]
   const int ld = a.d + 8;
-  const int cb = blockIdx.x, hg = blockIdx.y;
-  const int col0 = cb * C;
+  const int hg = blockIdx.y;
   const int hp = a.hp;
-  // segment containing col0 (segments are kPad-token aligned in columns)
-  int lo = 0, hi = a.n_seg - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (a.seg_pad[mid] * hp <= col0) lo = mid;
-    else hi = mid - 1;
-  }
-  const int s = lo;
-  const int seg_len = a.seg_cu[s + 1] - a.seg_cu[s];
-  const int u0 = (col0 - a.seg_pad[s] * hp) / hp;
   const T* in = static_cast<const T*>(a.in);
   T* out = static_cast<T*>(a.out);
   constexpr int CH = 16 / sizeof(T);
   const int nch = a.d / CH;
-  for (int q = threadIdx.x; q < C * nch; q += 256) {
-    const int c = q / nch, ch = q % nch;
-    const int u = u0 + c / hp;
-    u32x4 v = u32x4{0, 0, 0, 0};
-    if (u < seg_len)
-      v = *reinterpret_cast<const u32x4*>(
-          in + ((size_t)(a.seg_cu[s] + u) * a.heads + hg * hp + c % hp) * a.d + ch * CH);
-    *reinterpret_cast<u32x4*>(tile + c * ld + ch * CH) = v;
-  }
-  __syncthreads();
   const size_t stride = (size_t)a.pad_tokens * hp;
-  for (int q = threadIdx.x; q < a.d * (C / CH); q += 256) {
-    const int dd = q / (C / CH), ch = q % (C / CH);
-    T vals[CH];
-#pragma unroll
-    for (int e = 0; e < CH; ++e) {
-      const int pos = ch * CH + e;              // stored position in the 64 columns
-      const int src = (pos & ~15) | perm16(pos & 15);  // column held there
-      vals[e] = tile[src * ld + dd];
+  const long long n_cb = stride / C;
+  // column blocks, grid-stride (the whole workgroup takes the same blocks)
+  for (long long cb = blockIdx.x; cb < n_cb; cb += gridDim.x) {
+    const long long col0 = cb * C;
+    // segment containing col0 (segments are kPad-token aligned in columns)
+    int lo = 0, hi = a.n_seg - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((long long)a.seg_pad[mid] * hp <= col0) lo = mid;
+      else hi = mid - 1;
     }
-    *reinterpret_cast<u32x4*>(out + ((size_t)hg * a.d + dd) * stride + col0 + ch * CH) =
-        *reinterpret_cast<const u32x4*>(vals);
+    const int s = lo;
+    const int seg_len = a.seg_cu[s + 1] - a.seg_cu[s];
+    const int u0 = (int)((col0 - (long long)a.seg_pad[s] * hp) / hp);
+    for (int q = threadIdx.x; q < C * nch; q += kAuxThreads) {
+      const int c = q / nch, ch = q % nch;
+      const int u = u0 + c / hp;
+      u32x4 v = u32x4{0, 0, 0, 0};
+      if (u < seg_len)
+        v = *reinterpret_cast<const u32x4*>(
+            in + ((size_t)(a.seg_cu[s] + u) * a.heads + hg * hp + c % hp) * a.d + ch * CH);
+      *reinterpret_cast<u32x4*>(tile + c * ld + ch * CH) = v;
+    }
+    __syncthreads();
+    for (int q = threadIdx.x; q < a.d * (C / CH); q += kAuxThreads) {
+      const int dd = q / (C / CH), ch = q % (C / CH);
+      T vals[CH];
+#pragma unroll
+      for (int e = 0; e < CH; ++e) {
+        const int pos = ch * CH + e;                     // stored position in the 64 columns
+        const int src = (pos & ~15) | perm16(pos & 15);  // column held there
+        vals[e] = tile[src * ld + dd];
+      }
+      *reinterpret_cast<u32x4*>(out + ((size_t)hg * a.d + dd) * stride + col0 + ch * CH) =
+          *reinterpret_cast<const u32x4*>(vals);
+    }
+    __syncthreads();  // the tile is refilled by the next column block
   }
 }
 
 hipError_t launch_transpose(const TransposeArgs& a, int dtype, hipStream_t s) {
   const int cols = a.pad_tokens * a.hp;
   if (cols == 0) return hipSuccess;
-  dim3 grid(cols / 64, a.heads / a.hp);
+  // one workgroup per 64 columns, up to the cap of a dispatch
+  const long long blocks = (long long)cols / 64;
+  dim3 grid((unsigned)(blocks < kAuxMaxBlocks ? blocks : kAuxMaxBlocks), a.heads / a.hp);
   const size_t esz = dtype == 1 ? 2 : 4;
   const size_t smem = 64 * (size_t)(a.d + 8) * esz;
-  if (dtype == 1) hipLaunchKernelGGL(transpose_kernel<bf16>, grid, dim3(256), smem, s, a);
-  else hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(256), smem, s, a);
+  if (dtype == 1) hipLaunchKernelGGL(transpose_kernel<bf16>, grid, dim3(kAuxThreads), smem, s, a);
+  else hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(kAuxThreads), smem, s, a);
   return hipGetLastError();
 }
 
@@ -398,29 +406,33 @@ hipError_t launch_transpose(const TransposeArgs& a, int dtype, hipStream_t s) {
 // delta[h][t] = sum_c dout[t][h][c] * out[t][h][c]; 16 lanes per row.
 
 template <typename T>
-__global__ __launch_bounds__(256) void row_dot_kernel(const T* dout, const T* out, float* delta,
-                                                      int tokens, int heads, int d) {
+__global__ __launch_bounds__(kAuxThreads) void row_dot_kernel(const T* dout, const T* out,
+                                                              float* delta, int tokens, int heads,
+                                                              int d) {
   constexpr int CH = 16 / sizeof(T);
   const int lanes = d / CH;  // 16 (bf16, d=128) ... 4 (fp32, d=64)... per row
-  const int gid = blockIdx.x * 256 + threadIdx.x;
-  const int row = gid / 16, part = gid % 16;
-  const bool ok = row < tokens * heads;
-  float acc = 0.f;
-  if (ok) {
+  const long long rows = (long long)tokens * heads;
+  // 16 consecutive threads per row; the stride is a multiple of 16, so the
+  // 16 lanes of a row stay together (and leave the loop together)
+  for (long long gid = aux_first(blockIdx.x, threadIdx.x); gid < rows * 16;
+       gid += aux_stride(gridDim.x)) {
+    const long long row = gid / 16;
+    const int part = (int)(gid % 16);
+    float acc = 0.f;
     const size_t base = (size_t)row * d;
     for (int ch = part; ch < lanes; ch += 16) {
-      T a[CH], b[CH];
-      *reinterpret_cast<u32x4*>(a) = *reinterpret_cast<const u32x4*>(dout + base + ch * CH);
-      *reinterpret_cast<u32x4*>(b) = *reinterpret_cast<const u32x4*>(out + base + ch * CH);
+      T x[CH], y[CH];
+      *reinterpret_cast<u32x4*>(x) = *reinterpret_cast<const u32x4*>(dout + base + ch * CH);
+      *reinterpret_cast<u32x4*>(y) = *reinterpret_cast<const u32x4*>(out + base + ch * CH);
 #pragma unroll
-      for (int e = 0; e < CH; ++e) acc += to_f32(a[e]) * to_f32(b[e]);
+      for (int e = 0; e < CH; ++e) acc += to_f32(x[e]) * to_f32(y[e]);
     }
-  }
 #pragma unroll
-  for (int off = 8; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 16);
-  if (ok && part == 0) {
-    const int t = row / heads, h = row % heads;
-    delta[(size_t)h * tokens + t] = acc;
+    for (int off = 8; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 16);
+    if (part == 0) {
+      const long long t = row / heads, h = row % heads;
+      delta[h * tokens + t] = acc;
+    }
   }
 }
 
@@ -428,13 +440,13 @@ hipError_t launch_row_dot(const void* dout, const void* out, float* delta, int t
                           int d, int dtype, hipStream_t s) {
   const long long rows = (long long)tokens * heads;
   if (rows == 0) return hipSuccess;
-  const int grid = (int)((rows * 16 + 255) / 256);
+  const int grid = (int)aux_blocks(rows * 16);
   if (dtype == 1)
-    hipLaunchKernelGGL(row_dot_kernel<bf16>, dim3(grid), dim3(256), 0, s,
+    hipLaunchKernelGGL(row_dot_kernel<bf16>, dim3(grid), dim3(kAuxThreads), 0, s,
                        static_cast<const bf16*>(dout), static_cast<const bf16*>(out), delta,
                        tokens, heads, d);
   else
-    hipLaunchKernelGGL(row_dot_kernel<float>, dim3(grid), dim3(256), 0, s,
+    hipLaunchKernelGGL(row_dot_kernel<float>, dim3(grid), dim3(kAuxThreads), 0, s,
                        static_cast<const float*>(dout), static_cast<const float*>(out), delta,
                        tokens, heads, d);
   return hipGetLastError();
@@ -446,39 +458,40 @@ hipError_t launch_row_dot(const void* dout, const void* out, float* delta, int t
 // 16 lanes per (row, head), 8 (d = 128) or 4 (d = 64) elements per lane.
 
 template <typename T>
-__global__ __launch_bounds__(256) void lse_merge_kernel(int splits, int rows, int heads, int d,
-                                                        const float* o_parts,
-                                                        const float* lse_parts, T* o_out,
-                                                        float* lse_out) {
-  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
-  const long long item = gid / 16;
-  const int part = (int)(gid % 16);
-  if (item >= (long long)rows * heads) return;
-  const int r = (int)(item / heads), h = (int)(item % heads);
-  const size_t lstride = (size_t)heads * rows;
-  const size_t li = (size_t)h * rows + r;
-  float mx = -INFINITY;
-  for (int k = 0; k < splits; ++k) mx = fmaxf(mx, lse_parts[k * lstride + li]);
-  const int per = d / 16;  // elements per lane
-  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  float wsum = 0.f;
-  if (mx != -INFINITY) {
-    const size_t ostride = (size_t)rows * heads * d;
-    const size_t ob = ((size_t)r * heads + h) * d + part * per;
-    for (int k = 0; k < splits; ++k) {
-      const float lk = lse_parts[k * lstride + li];
-      const float wk = lk == -INFINITY ? 0.f : fast_exp2((lk - mx) * kLog2e);
-      wsum += wk;
-      if (wk != 0.f) {
-        const float* src = o_parts + k * ostride + ob;
-        for (int e = 0; e < per; ++e) acc[e] += wk * src[e];
+__global__ __launch_bounds__(kAuxThreads) void lse_merge_kernel(int splits, int rows, int heads,
+                                                                int d, const float* o_parts,
+                                                                const float* lse_parts, T* o_out,
+                                                                float* lse_out) {
+  const long long n = (long long)rows * heads * 16;
+  for (long long gid = aux_first(blockIdx.x, threadIdx.x); gid < n; gid += aux_stride(gridDim.x)) {
+    const long long item = gid / 16;
+    const int part = (int)(gid % 16);
+    const long long r = item / heads, h = item % heads;
+    const size_t lstride = (size_t)heads * rows;
+    const size_t li = (size_t)h * rows + r;
+    float mx = -INFINITY;
+    for (int k = 0; k < splits; ++k) mx = fmaxf(mx, lse_parts[k * lstride + li]);
+    const int per = d / 16;  // elements per lane
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    float wsum = 0.f;
+    if (mx != -INFINITY) {
+      const size_t ostride = (size_t)rows * heads * d;
+      const size_t ob = ((size_t)r * heads + h) * d + part * per;
+      for (int k = 0; k < splits; ++k) {
+        const float lk = lse_parts[k * lstride + li];
+        const float wk = lk == -INFINITY ? 0.f : fast_exp2((lk - mx) * kLog2e);
+        wsum += wk;
+        if (wk != 0.f) {
+          const float* src = o_parts + k * ostride + ob;
+          for (int e = 0; e < per; ++e) acc[e] += wk * src[e];
+        }
       }
     }
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    T* dst = o_out + ((size_t)r * heads + h) * d + part * per;
+    for (int e = 0; e < per; ++e) dst[e] = from_f32<T>(acc[e] * inv);
+    if (part == 0) lse_out[li] = mx == -INFINITY ? -INFINITY : mx + fast_log2(wsum) * kLn2;
   }
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  T* dst = o_out + ((size_t)r * heads + h) * d + part * per;
-  for (int e = 0; e < per; ++e) dst[e] = from_f32<T>(acc[e] * inv);
-  if (part == 0) lse_out[li] = mx == -INFINITY ? -INFINITY : mx + fast_log2(wsum) * kLn2;
 }
 
 hipError_t launch_lse_merge(int splits, int rows, int heads, int d, int out_dtype,
@@ -486,12 +499,12 @@ hipError_t launch_lse_merge(int splits, int rows, int heads, int d, int out_dtyp
                             float* lse_out, hipStream_t s) {
   const long long n = (long long)rows * heads * 16;
   if (n == 0) return hipSuccess;
-  const int grid = (int)((n + 255) / 256);
+  const int grid = (int)aux_blocks(n);
   if (out_dtype == 1)
-    hipLaunchKernelGGL(lse_merge_kernel<bf16>, dim3(grid), dim3(256), 0, s, splits, rows, heads,
+    hipLaunchKernelGGL(lse_merge_kernel<bf16>, dim3(grid), dim3(kAuxThreads), 0, s, splits, rows, heads,
                        d, o_parts, lse_parts, static_cast<bf16*>(o_out), lse_out);
   else
-    hipLaunchKernelGGL(lse_merge_kernel<float>, dim3(grid), dim3(256), 0, s, splits, rows, heads,
+    hipLaunchKernelGGL(lse_merge_kernel<float>, dim3(grid), dim3(kAuxThreads), 0, s, splits, rows, heads,
                        d, o_parts, lse_parts, static_cast<float*>(o_out), lse_out);
   return hipGetLastError();
 }

@@ -195,6 +195,16 @@ int validate_problem(const tree_attn_problem* p, bool need_device, Shape& s) {
   if (s.k_items_replay * s.hkv > lim || s.part_rows > lim)
     return TREE_ATTN_ERR_INVALID;
   s.col_splits = choose_col_splits(s);
+  // every attention launch must fit one dispatch: at most 2^32 - 1
+  // work-items (workgroups x threads), counting the XCD round-up
+  const long long n_hg = s.hq / s.hp;
+  const long long dispatch_max = (long long)UINT32_MAX;
+  const long long q_prefill = std::max(s.q_items_prefill * 512, s.wq_items_prefill * 768);
+  const long long q_replay = std::max(s.q_items_replay * s.col_splits * 512, s.wq_items_replay * 768);
+  if ((q_prefill + 8 * 768) * n_hg > dispatch_max || (q_replay + 8 * 768) * n_hg > dispatch_max)
+    return TREE_ATTN_ERR_INVALID;
+  if ((std::max(s.k_items_prefill, s.k_items_replay) + 8) * s.hkv * 512 > dispatch_max)
+    return TREE_ATTN_ERR_INVALID;
   // tile copies address a head group's slice of a transposed copy with a
   // 32-bit byte offset
   const long long slice = (long long)s.d * std::max(s.p_pad, s.r_pad) * s.hp * (long long)s.esz;

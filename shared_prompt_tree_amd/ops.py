@@ -97,6 +97,18 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _used_on(stream, *tensors):
+    """Tensors allocated here come from torch's caching allocator on the
+    current stream.  When the library runs on another stream, mark them as
+    used there, so their memory is not handed out again before that stream's
+    work has finished."""
+    if stream is None or stream == torch.cuda.current_stream(stream.device):
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
+
+
 class TreeProblem:
     """Offsets and shapes of a batch of replay trees, on host and device.
 
@@ -213,28 +225,38 @@ def _workspace(problem, op, device):
 def tree_attn_prefill(problem, q_p, k_p, v_p, o_p=None, lse_p=None, stream=None):
     """Causal prompt prefill.  Returns (o_p, lse_p)."""
     dev = q_p.device
-    o_p = torch.empty_like(q_p) if o_p is None else o_p
-    lse_p = (torch.empty(problem.hq, problem.prompt_tokens, dtype=torch.float32, device=dev)
-             if lse_p is None else lse_p)
+    made = []
+    if o_p is None:
+        o_p = torch.empty_like(q_p)
+        made.append(o_p)
+    if lse_p is None:
+        lse_p = torch.empty(problem.hq, problem.prompt_tokens, dtype=torch.float32, device=dev)
+        made.append(lse_p)
     _check_tensors(problem, q_p=q_p, k_p=k_p, v_p=v_p, o_p=o_p, lse_p=lse_p)
     ws, n = _workspace(problem, OP_PREFILL, dev)
     _check("tree_attn_prefill", library().tree_attn_prefill(
         ctypes.byref(problem.c), _ptr(q_p), _ptr(k_p), _ptr(v_p), _ptr(o_p), _ptr(lse_p),
         _ptr(ws), n, _stream(stream)))
+    _used_on(stream, ws, *made)
     return o_p, lse_p
 
 
 def tree_attn_replay_fwd(problem, k_p, v_p, q_r, k_r, v_r, o_r=None, lse_r=None, stream=None):
     """Response replay forward.  Returns (o_r, lse_r)."""
     dev = q_r.device
-    o_r = torch.empty_like(q_r) if o_r is None else o_r
-    lse_r = (torch.empty(problem.hq, problem.resp_tokens, dtype=torch.float32, device=dev)
-             if lse_r is None else lse_r)
+    made = []
+    if o_r is None:
+        o_r = torch.empty_like(q_r)
+        made.append(o_r)
+    if lse_r is None:
+        lse_r = torch.empty(problem.hq, problem.resp_tokens, dtype=torch.float32, device=dev)
+        made.append(lse_r)
     _check_tensors(problem, k_p=k_p, v_p=v_p, q_r=q_r, k_r=k_r, v_r=v_r, o_r=o_r, lse_r=lse_r)
     ws, n = _workspace(problem, OP_REPLAY_FWD, dev)
     _check("tree_attn_replay_fwd", library().tree_attn_replay_fwd(
         ctypes.byref(problem.c), _ptr(k_p), _ptr(v_p), _ptr(q_r), _ptr(k_r), _ptr(v_r),
         _ptr(o_r), _ptr(lse_r), _ptr(ws), n, _stream(stream)))
+    _used_on(stream, ws, *made)
     return o_r, lse_r
 
 
@@ -243,10 +265,12 @@ def tree_attn_replay_bwd(problem, k_p, v_p, q_r, k_r, v_r, o_r, lse_r, do_r, see
     """Replay backward.  Returns (dq_r, dk_r, dv_r, dk_p_seed, dv_p_seed);
     the seeds are None when ``seeds`` is False (detached prompt)."""
     dev = q_r.device
+    made = ()
     if out is None:
         out = (torch.empty_like(q_r), torch.empty_like(k_r), torch.empty_like(v_r),
                torch.empty(k_p.shape, dtype=torch.float32, device=dev) if seeds else None,
                torch.empty(v_p.shape, dtype=torch.float32, device=dev) if seeds else None)
+        made = out
     dq_r, dk_r, dv_r, dks, dvs = out
     _check_tensors(problem, k_p=k_p, v_p=v_p, q_r=q_r, k_r=k_r, v_r=v_r, o_r=o_r, lse_r=lse_r,
                    do_r=do_r, dq_r=dq_r, dk_r=dk_r, dv_r=dv_r, dk_p_seed=dks, dv_p_seed=dvs)
@@ -255,6 +279,7 @@ def tree_attn_replay_bwd(problem, k_p, v_p, q_r, k_r, v_r, o_r, lse_r, do_r, see
         ctypes.byref(problem.c), _ptr(k_p), _ptr(v_p), _ptr(q_r), _ptr(k_r), _ptr(v_r),
         _ptr(o_r), _ptr(lse_r), _ptr(do_r), _ptr(dq_r), _ptr(dk_r), _ptr(dv_r), _ptr(dks),
         _ptr(dvs), _ptr(ws), n, _stream(stream)))
+    _used_on(stream, ws, *made)
     return dq_r, dk_r, dv_r, dks, dvs
 
 
@@ -262,8 +287,10 @@ def tree_attn_prefill_bwd(problem, q_p, k_p, v_p, o_p, lse_p, do_p, dk_p_seed=No
                           dv_p_seed=None, out=None, stream=None):
     """Prefill backward with the replay seeds.  Returns (dq_p, dk_p, dv_p)."""
     dev = q_p.device
+    made = ()
     if out is None:
         out = (torch.empty_like(q_p), torch.empty_like(k_p), torch.empty_like(v_p))
+        made = out
     dq_p, dk_p, dv_p = out
     _check_tensors(problem, q_p=q_p, k_p=k_p, v_p=v_p, o_p=o_p, lse_p=lse_p, do_p=do_p,
                    dk_p_seed=dk_p_seed, dv_p_seed=dv_p_seed, dq_p=dq_p, dk_p=dk_p, dv_p=dv_p)
@@ -272,6 +299,7 @@ def tree_attn_prefill_bwd(problem, q_p, k_p, v_p, o_p, lse_p, do_p, dk_p_seed=No
         ctypes.byref(problem.c), _ptr(q_p), _ptr(k_p), _ptr(v_p), _ptr(o_p), _ptr(lse_p),
         _ptr(do_p), _ptr(dk_p_seed), _ptr(dv_p_seed), _ptr(dq_p), _ptr(dk_p), _ptr(dv_p),
         _ptr(ws), n, _stream(stream)))
+    _used_on(stream, ws, *made)
     return dq_p, dk_p, dv_p
 
 
@@ -282,14 +310,19 @@ def lse_merge(o_parts, lse_parts, out_dtype=torch.float32, o_out=None, lse_out=N
     dev = o_parts.device
     _req("o_parts", o_parts, (s, rows, heads, d), torch.float32, dev)
     _req("lse_parts", lse_parts, (s, heads, rows), torch.float32, dev)
-    o_out = torch.empty(rows, heads, d, dtype=out_dtype, device=dev) if o_out is None else o_out
-    lse_out = (torch.empty(heads, rows, dtype=torch.float32, device=dev)
-               if lse_out is None else lse_out)
+    made = []
+    if o_out is None:
+        o_out = torch.empty(rows, heads, d, dtype=out_dtype, device=dev)
+        made.append(o_out)
+    if lse_out is None:
+        lse_out = torch.empty(heads, rows, dtype=torch.float32, device=dev)
+        made.append(lse_out)
     _req("o_out", o_out, (rows, heads, d), o_out.dtype, dev)
     _req("lse_out", lse_out, (heads, rows), torch.float32, dev)
     _check("lse_merge", library().lse_merge(
         s, rows, heads, d, _DTYPE_CODE[o_out.dtype], _ptr(o_parts), _ptr(lse_parts),
         _ptr(o_out), _ptr(lse_out), _stream(stream)))
+    _used_on(stream, *made)
     return o_out, lse_out
 
 

@@ -66,8 +66,50 @@ def rel_l2(x, ref):
     return e / n if n > 0 else e
 
 
-def compare(lib, ref, tol, names=OUT_NAMES, label=""):
-    errs = {}
+def _segments(tree, name):
+    """Row ranges of an output tensor that the per-segment check gates: the
+    prompt of each group for prompt tensors, each branch for response
+    tensors.  Returns (token axis, [(start, stop), ...])."""
+    cu = tree.prompt_cu if name.endswith("_p") else tree.resp_cu
+    axis = 1 if name.startswith("lse") else 0
+    return axis, [(int(a), int(b)) for a, b in zip(cu[:-1], cu[1:]) if b > a]
+
+
+# A segment whose reference norm is below this fraction of its share of the
+# whole tensor's norm (the tensor norm scaled by sqrt(segment size / tensor
+# size)) is compared against that share instead: its own norm is then a
+# cancellation residue, not a scale.
+SEG_FLOOR = 1e-2
+
+
+def segment_errors(x, ref, tree, name):
+    """Relative L2 of every (segment, head) block of one output tensor:
+    ||x - ref|| / max(||ref||, SEG_FLOOR * share), per group prompt or per
+    branch and per head.  Returns the worst value and where it occurred."""
+    axis, segs = _segments(tree, name)
+    n_tok = ref.shape[axis]
+    total = np.linalg.norm(ref)
+    worst, where = 0.0, None
+    heads = ref.shape[0] if axis == 1 else ref.shape[1]
+    for a, b in segs:
+        for h in range(heads):
+            if axis == 1:
+                xs, rs = x[h, a:b], ref[h, a:b]
+            else:
+                xs, rs = x[a:b, h], ref[a:b, h]
+            share = total * math.sqrt((b - a) / max(n_tok, 1) / heads)
+            den = max(np.linalg.norm(rs), SEG_FLOOR * share)
+            e = np.linalg.norm(xs - rs) / den if den > 0 else np.linalg.norm(xs)
+            if e > worst:
+                worst, where = e, (a, b, h)
+    return worst, where
+
+
+def compare(lib, ref, tol, names=OUT_NAMES, label="", tree=None):
+    """Relative L2 per output tensor, and (given the tree) per group prompt or
+    branch and head, so that a large-norm row cannot hide errors elsewhere.
+    Both must be within tol."""
+    errs, seg = {}, {}
     for k in names:
         a = host64(lib[k])
         if a.size == 0:
@@ -75,7 +117,13 @@ def compare(lib, ref, tol, names=OUT_NAMES, label=""):
             continue
         assert np.all(np.isfinite(a)), f"{label} {k}: non-finite values"
         errs[k] = rel_l2(a, ref[k])
+        if tree is not None:
+            seg[k] = segment_errors(a, np.asarray(ref[k], np.float64), tree, k)
     say(label, " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    if seg:
+        say(label, "worst segment:", " ".join(f"{k}={v[0]:.2e}" for k, v in seg.items()))
     bad = {k: v for k, v in errs.items() if not v <= tol}
     assert not bad, f"{label}: rel L2 above {tol}: {bad}"
+    bad = {k: v for k, v in seg.items() if not v[0] <= tol}
+    assert not bad, f"{label}: per-segment rel L2 above {tol} (start, stop, head): {bad}"
     return errs

@@ -92,6 +92,45 @@ def test_token_totals_beyond_int32_rejected(prompt, resp, heads):
         assert e.value.code == -1
 
 
+def test_attention_launch_dispatch_limit():
+    """A launch is one dispatch of at most 2^32 - 1 work-items.  MHA with 64
+    heads (64 head groups) and a prompt of 2^25 - 128 tokens passes every
+    other size check (tokens x Hq < 2^31, the transposed copy < 4 GiB) but its
+    prefill forward would need 64 x 131072 workgroups of 512 threads: it is
+    rejected on the host.  Half the heads fits."""
+    P = 2 ** 25 - 128
+    too_big = small_problem(prompt_cu=[0, P], group_branch_cu=[0, 0], resp_cu=[0],
+                            num_q_heads=64, num_kv_heads=64, head_dim=64)
+    with pytest.raises(ops.TreeAttnError) as e:
+        ops.tree_attn_workspace_size(too_big, ops.OP_PREFILL)
+    assert e.value.code == -1
+    fits = small_problem(prompt_cu=[0, P], group_branch_cu=[0, 0], resp_cu=[0],
+                         num_q_heads=32, num_kv_heads=32, head_dim=64)
+    assert ops.tree_attn_workspace_size(fits, ops.OP_PREFILL) > 0
+
+
+def test_aux_launch_math_at_the_largest_problem(tmp_path):
+    """The element-wise kernels (row dot, merge, seed and chunk sums,
+    transposed copies) launch a capped grid and walk their elements with a
+    64-bit grid-stride loop.  A host build of that geometry (grid_math.h, the
+    header the kernels use) checks it at tokens x Hq = 2^31 - 1 rows of 16
+    lanes each: the grid fits a dispatch, every element is visited, and the
+    16 lanes of a row stay in one pass."""
+    import shutil
+    import subprocess
+
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("no host C++ compiler")
+    exe = tmp_path / "grid_math_check"
+    subprocess.run([gxx, "-std=c++17", "-O1", "-I",
+                    os.path.join(ROOT, "shared_prompt_tree_amd", "csrc"),
+                    os.path.join(ROOT, "tests", "grid_math_check.cpp"), "-o", str(exe)],
+                   check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+
+
 def test_transposed_copy_offset_limit():
     """A head group's slice of a transposed copy is addressed with 32-bit
     byte offsets: head_dim * padded tokens * packed heads * element size must

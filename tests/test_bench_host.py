@@ -121,3 +121,36 @@ def test_summary_records_the_profiled_workload(tmp_profiles):
                     "rocprofv3 --pmc FETCH_SIZE -- python3 bench.py --workload long_mixed")
     with open(bench.traffic_file("long_mixed")) as f:
         assert json.load(f)["workload"] == "long_mixed"
+
+
+def test_per_launch_traffic_report(tmp_profiles):
+    """The roofline's per-launch record: the stored counters of each launch of
+    one step (two profiled steps, launches in call order), the algorithmic
+    bytes and the achieved bandwidth."""
+    from shared_prompt_tree_amd import workloads as wl
+
+    os.makedirs(bench.PROFILES)
+    rec = {"workload": "prompt_heavy",
+           "kernels": {"dkv": {"hbm_bytes_per_launch": 1,
+                               "source_hash": bench.kernel_source_hash("dkv"),
+                               "read_bytes": [10e9, 100e9, 12e9, 102e9],
+                               "write_bytes": [1e9, 2e9, 3e9, 4e9]}}}
+    with open(bench.traffic_file("prompt_heavy"), "w") as f:
+        json.dump(rec, f)
+    st = bench.stored_launch_traffic("dkv", "prompt_heavy")
+    assert st == [(11e9, 2e9), (101e9, 3e9)]
+    assert bench.stored_launch_traffic("dkv", "response_heavy") is None
+    tree = wl.make_tree(wl.SPECS["prompt_heavy"])
+    # prefill dK/dV: Q, dO (2 x 32768 x 32 x 128 x 2 B), LSE and D (2 x 32768
+    # x 32 x 4 B), K, V in and dK, dV out (4 x 32768 x 8 x 128 x 2 B), float32
+    # seeds in (2 x 32768 x 8 x 128 x 4 B)
+    want = 2 * 268435456 + 2 * 4194304 + 4 * 67108864 + 2 * 134217728
+    assert bench.algorithmic_bytes(tree, "dkv", "prefill_bwd") == want
+    launches = bench.launch_report(tree, "dkv", [2.0, 20.0], st)
+    assert [x["call"] for x in launches] == ["replay_bwd", "prefill_bwd"]
+    pre = launches[1]
+    assert pre["hbm_bytes"] == 104e9 and pre["hbm_gbps"] == round(104e9 / 20e-3 / 1e9, 1)
+    assert pre["hbm_over_algorithmic"] == round(104e9 / want, 2)
+    assert launches[0]["hbm_read_bytes"] == 11e9
+    none = bench.launch_report(tree, "dkv", [2.0, 20.0], None)
+    assert none[0]["hbm_bytes"] is None and none[0]["algorithmic_bytes"] > 0

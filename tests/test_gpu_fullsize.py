@@ -2,18 +2,26 @@
 outputs it can compute one by one, and against sum rules over everything.
 
 Sampled checks (float64 oracle, ``oracle.causal_unit`` on the flattened
-(P, R_i) sequence of the sampled branch):
+(P, R_i) sequence of a branch), each gated per row as well as over the
+sample, so that rows with a large norm cannot hide errors on others:
 * forward outputs O, LSE and the query gradient dQ of sampled rows: each
   depends on its own row only;
 * dK, dV of the last keys of sampled branches: only rows of that branch at
   or after the key read it, so the rows [k0, L) give the exact gradient;
-* (prompt-heavy shape) dK_P, dV_P of the last prompt keys: the prompt rows
-  after them plus every response row of every branch.
+* prompt dK_P, dV_P of chosen prompt keys of one group and kv head
+  (``oracle.causal_key_grads``): the prompt rows at or after the key plus
+  every response row of every branch of the group, for every query head of
+  the kv head (the sum over branches
+  of the AugTree paper, section 3.2, Eq. 2).  Prompt-heavy: the first 64 and
+  the last 32 prompt keys; response-heavy: all 256 prompt keys (the launch
+  cuts each group's prompt tiles into branch ranges, so this also covers the
+  partial seeds and their ordered sum); long-mixed: the last 64 prompt keys.
 Sum rules over all outputs: per group and kv head, sum_j dK_j = 0 and
 sum_j dV_j = sum of dO over the rows of the query heads that read it.
 """
 
 import math
+import multiprocessing as mp
 
 import numpy as np
 import pytest
@@ -21,7 +29,7 @@ import torch
 
 import oracle
 from shared_prompt_tree_amd import workloads as wl
-from tests._gpu import TOL, host64, make_case, rel_l2, run_library, say
+from tests._gpu import TOL, WORKERS, host64, make_case, rel_l2, run_library, say
 
 pytestmark = pytest.mark.gpu
 
@@ -57,6 +65,128 @@ def _sample_branches(tree, rng):
 
 def _group_of(tree, i):
     return int(np.searchsorted(tree.group_branch_cu, i, side="right") - 1)
+
+
+# ------------------------------------------------------------ prompt keys
+#
+# The rows that read a prompt key are spread over every branch of its group,
+# so the oracle's share is cut into units of rows (bounded work each) and run
+# in forked workers; the inputs of the one group and kv head are float64
+# host copies inherited by the workers.
+
+_KEYS = None
+_PAIRS_PER_UNIT = 200_000_000
+
+
+def _key_unit(args):
+    """dK, dV of the chosen prompt keys from one query head of one branch,
+    over the flattened rows [a, b) of that branch."""
+    from threadpoolctl import threadpool_limits
+
+    i, j, a, b, scale = args
+    d = _KEYS
+    first = i == d["b0"]
+    xq = np.concatenate([d["qp"][:, j], d["qr"][i][:, j]])
+    xk = np.concatenate([d["kp"], d["kr"][i]])
+    xv = np.concatenate([d["vp"], d["vr"][i]])
+    dop = d["dop"][:, j] if first else np.zeros_like(d["dop"][:, j])
+    xdo = np.concatenate([dop, d["dor"][i][:, j]])
+    with threadpool_limits(1):
+        return oracle.causal_key_grads(xq, xk, xv, xdo, scale, np.arange(a, b), d["keys"],
+                                       chunk=512)
+
+
+def prompt_key_grads(tree, t, g, kv, keys):
+    """Oracle dK_P, dV_P [len(keys), d] of prompt keys ``keys`` (positions in
+    group g's prompt) for kv head kv: every query head of kv, every branch of
+    g.  The prompt rows carry their upstream gradient in the group's first
+    branch only (exact: the backward is linear in dO), so later branches
+    contribute through their response rows alone."""
+    global _KEYS
+    rep = tree.hq // tree.hkv
+    hs = slice(kv * rep, (kv + 1) * rep)
+    p0, p1 = int(tree.prompt_cu[g]), int(tree.prompt_cu[g + 1])
+    b0, b1 = int(tree.group_branch_cu[g]), int(tree.group_branch_cu[g + 1])
+    P = p1 - p0
+    keys = np.asarray(keys)
+    data = {"b0": b0, "keys": keys, "qp": host64(t["q_p"][p0:p1, hs]),
+            "kp": host64(t["k_p"][p0:p1, kv]), "vp": host64(t["v_p"][p0:p1, kv]),
+            "dop": host64(t["do_p"][p0:p1, hs]), "qr": {}, "kr": {}, "vr": {}, "dor": {}}
+    units = []
+    scale = 1.0 / math.sqrt(tree.d)
+    for i in range(b0, b1):
+        r0, r1 = int(tree.resp_cu[i]), int(tree.resp_cu[i + 1])
+        data["qr"][i] = host64(t["q_r"][r0:r1, hs])
+        data["kr"][i] = host64(t["k_r"][r0:r1, kv])
+        data["vr"][i] = host64(t["v_r"][r0:r1, kv])
+        data["dor"][i] = host64(t["do_r"][r0:r1, hs])
+        L = P + r1 - r0
+        start = int(keys.min()) if i == b0 else P  # first row that can read a chosen key
+        for j in range(rep):
+            a = start
+            while a < L:  # rows [a, b) with about _PAIRS_PER_UNIT (row, key) pairs
+                b = min(L, a + max(1, _PAIRS_PER_UNIT // (a + 1)))
+                units.append((i, j, a, b, scale))
+                a = b
+    _KEYS = data
+    try:
+        with mp.get_context("fork").Pool(min(WORKERS, len(units))) as pool:
+            parts = pool.map(_key_unit, units, chunksize=1)
+    finally:
+        _KEYS = None
+    dk = sum(x[0] for x in parts)
+    dv = sum(x[1] for x in parts)
+    say(f"[full] prompt keys of group {g}, kv head {kv}: {len(keys)} keys, {len(units)} "
+        f"oracle units over {b1 - b0} branches x {rep} query heads")
+    return dk, dv
+
+
+# A sampled row whose reference norm is below this fraction of the sample's
+# median row norm is measured against that fraction instead: prompt row 0,
+# with a single visible key, has dQ = 0 exactly (its one dS is dP - D with
+# D = dP), and the GPU's value is the float32 rounding residue of that
+# difference, about 1.5e-5 of the median row on the prompt-heavy workload.
+ROW_FLOOR = 1e-2
+
+
+def _row_errors(a, b, kind):
+    """Error of each row of a sampled block: relative L2 of a (token, head)
+    vector of head_dim values, floored at ROW_FLOOR times the median row
+    norm; for LSE (one value per row, a logarithm) |x - x*| / max(1, |x*|)."""
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    if kind == "lse":
+        return np.abs(a - b).ravel() / np.maximum(1.0, np.abs(b).ravel())
+    a = a.reshape(-1, a.shape[-1])
+    b = b.reshape(a.shape)
+    den = np.linalg.norm(b, axis=1)
+    den = np.maximum(den, ROW_FLOOR * np.median(den))
+    return np.linalg.norm(a - b, axis=1) / den
+
+
+def _check_sampled(label, got, want):
+    for k in got:
+        if not got[k]:
+            continue
+        a = np.concatenate([x.ravel() for x in got[k]])
+        b = np.concatenate([x.ravel() for x in want[k]])
+        err = rel_l2(a, b)
+        kind = "lse" if k == "lse" else "vec"
+        rows = np.concatenate([_row_errors(x, y, kind) for x, y in zip(got[k], want[k])])
+        worst = int(np.argmax(rows))
+        say(f"[full] {label} sampled {k}: {len(a)} values, rel L2 {err:.2e}; "
+            f"{len(rows)} rows, worst row {rows[worst]:.2e}, median row "
+            f"{float(np.median(rows)):.2e}")
+        assert err <= TOL["bf16"], (k, err)
+        assert rows[worst] <= TOL["bf16"], (k, worst, rows[worst])
+
+
+PROMPT_KEYS = {
+    # (first keys, last keys) of group 0's prompt, one kv head
+    "prompt_heavy": (64, 32),
+    "response_heavy": (256, 0),
+    "long_mixed": (0, 64),
+}
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -133,35 +263,19 @@ def test_full_size(name):
         want["dk"].append(dk)
         want["dv"].append(dv)
 
-    if name == "prompt_heavy":
-        # last prompt keys: prompt rows after them and every response row
-        g, kv, n = 0, int(rng.integers(0, tree.hkv)), 32
-        P = int(tree.prompt_cu[1])
-        b0, b1 = int(tree.group_branch_cu[0]), int(tree.group_branch_cu[1])
-        dk = 0
-        dv = 0
-        for h in range(kv * rep, (kv + 1) * rep):
-            for i in range(b0, b1):
-                f = _flat(tree, t, g, i, h)
-                L = f["q"].shape[0]
-                rows = np.arange(P - n if i == b0 else P, L)
-                _, _, _, dk_h, dv_h = oracle.causal_unit(f["q"], f["k"], f["v"], f["do"], scale,
-                                                         rows=rows)
-                dk = dk + dk_h[P - n:P]
-                dv = dv + dv_h[P - n:P]
-        got["dk"].append(host64(lib["dk_p"][P - n:P, kv]))
-        got["dv"].append(host64(lib["dv_p"][P - n:P, kv]))
-        want["dk"].append(dk)
-        want["dv"].append(dv)
+    # prompt dK_P, dV_P of chosen prompt keys of group 0, summed over every
+    # branch of the group and every query head of the kv head
+    n_first, n_last = PROMPT_KEYS[name]
+    P = int(tree.prompt_cu[1])
+    keys = np.array(sorted(set(range(min(n_first, P))) | set(range(max(0, P - n_last), P))))
+    kv = int(rng.integers(0, tree.hkv))
+    dk, dv = prompt_key_grads(tree, t, 0, kv, keys)
+    got["dk_p"] = [host64(lib["dk_p"][keys, kv])]
+    got["dv_p"] = [host64(lib["dv_p"][keys, kv])]
+    want["dk_p"] = [dk]
+    want["dv_p"] = [dv]
 
-    for k in got:
-        if not got[k]:
-            continue
-        a = np.concatenate([x.ravel() for x in got[k]])
-        b = np.concatenate([x.ravel() for x in want[k]])
-        err = rel_l2(a, b)
-        say(f"[full] {name} sampled {k}: {len(a)} values, rel L2 {err:.2e}")
-        assert err <= TOL["bf16"], (k, err)
+    _check_sampled(name, got, want)
 
     # sum rules over every output, float64 on the GPU
     worst_k = worst_v = 0.0
@@ -207,9 +321,4 @@ def test_wide_forward_tiles():
         want["o"].append(o)
         want["lse"].append(lse)
         want["dq"].append(dq)
-    for k in got:
-        a = np.concatenate([x.ravel() for x in got[k]])
-        b = np.concatenate([x.ravel() for x in want[k]])
-        err = rel_l2(a, b)
-        say(f"[wide] sampled {k}: {len(a)} values, rel L2 {err:.2e}")
-        assert err <= TOL["bf16"], (k, err)
+    _check_sampled("wide prefill", got, want)

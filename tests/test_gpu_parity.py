@@ -30,14 +30,14 @@ def test_tiny_f32_full():
     spec = wl.SPECS["tiny"]
     tree = wl.make_tree(spec)
     _, _, lib, ref = _case(tree, spec.seed, spec.value_scale, "tiny")
-    compare(lib, ref, TOL["f32"], label="tiny")
+    compare(lib, ref, TOL["f32"], label="tiny", tree=tree)
 
 
 def test_small_bf16_full():
     spec = wl.SPECS["small"]
     tree = wl.make_tree(spec)
     _, _, lib, ref = _case(tree, spec.seed, 1.0, "small")
-    compare(lib, ref, TOL["bf16"], label="small")
+    compare(lib, ref, TOL["bf16"], label="small", tree=tree)
 
 
 # Oracle-sized versions of the large shapes: the same heads, head_dim and
@@ -50,11 +50,21 @@ REDUCED = {
 }
 
 
+# Replay launches of at least 1024 workgroups with 384-row tiles take the
+# 12-wave forward kernel, which the large configs use for their whole replay
+# forward: 64 branches of 200 tokens (3 tiles of 96 tokens x 4 packed heads
+# each) x 8 head groups = 1536 workgroups; and a longer prompt with 48
+# branches of 300 (4 tiles each) = 1536.  Prompts under 1024 keys are not
+# cut into chunks, so the prompt column runs inside the 12-wave kernel too.
+REDUCED["response_heavy 12-wave"] = wl.Tree([256], [[200] * 64], 32, 8, 128, "bf16")
+REDUCED["prompt column 12-wave"] = wl.Tree([1000], [[300] * 47 + [61]], 32, 8, 128, "bf16")
+
+
 @pytest.mark.parametrize("name", sorted(REDUCED))
 def test_reduced_shapes_full(name):
     tree = REDUCED[name]
     _, _, lib, ref = _case(tree, 7, 1.0, name)
-    compare(lib, ref, TOL["bf16"], label=name)
+    compare(lib, ref, TOL["bf16"], label=name, tree=tree)
 
 
 EDGE = {
@@ -109,7 +119,7 @@ def test_edge_cases(name):
     tree = EDGE[name]
     vs = 0.125 if tree.dtype == "f32" else 1.0
     _, _, lib, ref = _case(tree, 11, vs, name)
-    compare(lib, ref, TOL[tree.dtype], label=name)
+    compare(lib, ref, TOL[tree.dtype], label=name, tree=tree)
 
 
 @pytest.mark.parametrize("dtype,scale", [("bf16", 3.0), ("f32", 3.0)])
@@ -120,7 +130,7 @@ def test_peaked_scores(dtype, scale):
     maximum grows by more than 2^8)."""
     tree = wl.Tree([700, 90], [[300, 129], [260]], 8, 2, 128 if dtype == "bf16" else 64, dtype)
     _, _, lib, ref = _case(tree, 13, scale, f"peaked x{scale}")
-    compare(lib, ref, TOL[dtype], label=f"peaked {dtype}")
+    compare(lib, ref, TOL[dtype], label=f"peaked {dtype}", tree=tree)
 
 
 def _random_tree(seed):
@@ -148,7 +158,7 @@ def test_random_trees(seed):
     tree = _random_tree(1000 + seed)
     vs = 0.125 if tree.dtype == "f32" else 1.0
     _, _, lib, ref = _case(tree, 50 + seed, vs, f"random {seed}")
-    compare(lib, ref, TOL[tree.dtype], label=f"random {seed}")
+    compare(lib, ref, TOL[tree.dtype], label=f"random {seed}", tree=tree)
 
 
 def _random_split_tree(seed):
@@ -174,7 +184,7 @@ def _random_split_tree(seed):
 def test_random_split_trees(seed):
     tree = _random_split_tree(2000 + seed)
     _, _, lib, ref = _case(tree, 70 + seed, 1.0, f"random split {seed}")
-    compare(lib, ref, TOL["bf16"], label=f"random split {seed}")
+    compare(lib, ref, TOL["bf16"], label=f"random split {seed}", tree=tree)
 
 
 def test_zero_prompt_upstream_gradient():
@@ -183,7 +193,7 @@ def test_zero_prompt_upstream_gradient():
     _, _, lib, ref = _case(tree, 5, 1.0, "dO_P=0", zero_do_p=True)
     assert float(lib["dq_p"].abs().max()) == 0.0
     names = [n for n in ("o_p", "lse_p", "o_r", "lse_r", "dk_p", "dv_p", "dq_r", "dk_r", "dv_r")]
-    compare(lib, ref, TOL["bf16"], names=names, label="dO_P=0")
+    compare(lib, ref, TOL["bf16"], names=names, label="dO_P=0", tree=tree)
 
 
 def test_detached_prompt_seeds():
@@ -197,7 +207,8 @@ def test_detached_prompt_seeds():
     for k in ("q_r", "k_r", "v_r", "do_r"):
         ti[k] = t[k][:0]
     ref = run_oracle(prompt_only, ti)
-    compare(lib, ref, TOL["bf16"], names=("dq_p", "dk_p", "dv_p"), label="detached")
+    compare(lib, ref, TOL["bf16"], names=("dq_p", "dk_p", "dv_p"), label="detached",
+            tree=tree)
 
 
 def test_detached_prompt_seeds_split():
@@ -210,7 +221,8 @@ def test_detached_prompt_seeds_split():
     for k in ("q_r", "k_r", "v_r", "do_r"):
         ti[k] = t[k][:0]
     ref = run_oracle(prompt_only, ti)
-    compare(lib, ref, TOL["bf16"], names=("dq_p", "dk_p", "dv_p"), label="detached split")
+    compare(lib, ref, TOL["bf16"], names=("dq_p", "dk_p", "dv_p"), label="detached split",
+            tree=tree)
 
 
 def test_deterministic():

@@ -36,6 +36,17 @@ MUTATIONS = {
                           "w = np.exp(lse[None] - lse_parts)"),
     "merge normaliser": ("lse = np.logaddexp.reduce(lse_parts, axis=0)",
                          "lse = np.max(lse_parts, axis=0)"),
+    # causal_key_grads (prompt-key gradients from a subset of rows)
+    "key grads: diagonal excluded": (
+        "tail[np.arange(int(r[0]) + 1, kmax)[None, :] > r[:, None]] = -np.inf",
+        "tail[np.arange(int(r[0]) + 1, kmax)[None, :] >= r[:, None]] = -np.inf"),
+    "key grads: D term dropped": ("dsk = pk * (g @ xv[keys].T - dd)",
+                                  "dsk = pk * (g @ xv[keys].T)"),
+    "key grads: scale dropped from dK": ("dk += scale * (dsk.T @ xq[r])",
+                                         "dk += (dsk.T @ xq[r])"),
+    "key grads: scores not scaled": ("s *= scale", "s *= 1.0"),
+    "key grads: wrong key column": ("pk[:, seen] = s[:, keys[seen]]",
+                                    "pk[:, seen] = s[:, keys[seen] - 1]"),
 }
 
 
@@ -63,6 +74,16 @@ def pins_hold(mod):
             for k in OUTPUTS:
                 if not np.allclose(got[k], ref[k], rtol=1e-9, atol=1e-10):
                     return False
+    # prompt-key gradients from a subset of rows against torch autograd
+    from tests.test_oracle_pins import _sdpa_key_grads
+    rng = np.random.default_rng(2)
+    q, k, v, do = (rng.standard_normal((30, 4)) for _ in range(4))
+    rows, keys = np.arange(9, 30), np.array([0, 8, 9, 10, 29])
+    with np.errstate(all="ignore"):
+        dk, dv = mod.causal_key_grads(q, k, v, do, 0.7, rows, keys, chunk=4)
+    rk, rv = _sdpa_key_grads(q, k, v, do, 0.7, rows, keys)
+    if not (np.allclose(dk, rk, atol=1e-10) and np.allclose(dv, rv, atol=1e-10)):
+        return False
     # merge check: two halves of a key set merge to the whole
     rng = np.random.default_rng(1)
     q, k, v = (rng.standard_normal((6, 4)) for _ in range(3))

@@ -232,6 +232,35 @@ def test_single_branch_is_plain_causal_attention():
     np.testing.assert_allclose(r["dv_r"], dv[10:], atol=1e-12)
 
 
+def _sdpa_key_grads(q, k, v, do, scale, rows, keys):
+    """dK, dV of the chosen keys from torch float64 causal
+    scaled_dot_product_attention and autograd, with the upstream gradient
+    zeroed outside the chosen rows (the loss is linear in dO)."""
+    tq, tk, tv = (torch.tensor(x[None], requires_grad=True) for x in (q, k, v))
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True, scale=scale)
+    g = np.zeros_like(do)
+    g[rows] = do[rows]
+    (o * torch.tensor(g[None])).sum().backward()
+    return tk.grad[0].numpy()[keys], tv.grad[0].numpy()[keys]
+
+
+@pytest.mark.parametrize("rows,keys,chunk", [
+    (np.arange(90), np.arange(90), 17),                          # every row and key
+    (np.arange(40, 90), np.array([0, 3, 39, 40, 41, 89]), 8),    # keys on both sides of row 40
+    (np.array([5, 6, 50, 89]), np.array([6, 50, 60, 2]), 3),     # sparse rows, a key no row sees
+])
+def test_key_gradients_match_sdpa_autograd(rows, keys, chunk):
+    """oracle.causal_key_grads (prompt-key gradients from a subset of rows,
+    used by the full-size GPU checks) against torch's causal
+    scaled_dot_product_attention with autograd, float64."""
+    rng = np.random.default_rng(12)
+    q, k, v, do = (rng.standard_normal((90, 16)) for _ in range(4))
+    dk, dv = oracle.causal_key_grads(q, k, v, do, 0.3, rows, keys, chunk=chunk)
+    rk, rv = _sdpa_key_grads(q, k, v, do, 0.3, rows, keys)
+    np.testing.assert_allclose(dk, rk, atol=1e-12)
+    np.testing.assert_allclose(dv, rv, atol=1e-12)
+
+
 def sum_rules(tree, t, r):
     """Per group and kv head: sum_j dK_j = 0 and sum_j dV_j = sum of dO over
     the rows of the q-heads that read that kv head.  Each softmax row's dS
