@@ -27,8 +27,10 @@
  * gradient seeds and merge partials are always float32.  Matrix products
  * accumulate in float32.
  * Memory.  Every tensor pointer is caller-owned device memory with a
- * 16-byte aligned base.  The library allocates no device memory.  Scratch
- * space comes from the caller through (ws, ws_bytes), sized by
+ * 16-byte aligned base.  The library allocates no device memory (apart from
+ * the static scratch array of tree_attn_replay_fwd_noalloc, which comes with
+ * the code object on each GPU).  Scratch space comes from the caller through
+ * (ws, ws_bytes), sized by
  * tree_attn_workspace_size(); its contents need not be preserved between
  * calls.  Host arrays (*_h) are read during the call only; device arrays
  * (*_d) and every tensor must stay valid until the enqueued work finishes.
@@ -48,7 +50,8 @@
  * checked on the host before any HIP call, so a rejected call enqueues
  * nothing and writes nothing.  TREE_ATTN_ERR_HIP reports a failed launch.
  * The library holds no global mutable state apart from the per-thread
- * timing hook below, and may be called from several host threads.
+ * timing hook below and the per-GPU static scratch of
+ * tree_attn_replay_fwd_noalloc, and may be called from several host threads.
  */
 #ifndef TREE_ATTN_H_
 #define TREE_ATTN_H_
@@ -72,7 +75,9 @@ typedef enum {
   TREE_ATTN_ERR_INVALID = -1,     /* null pointer, bad offsets, bad shape */
   TREE_ATTN_ERR_UNSUPPORTED = -2, /* dtype or head_dim not supported */
   TREE_ATTN_ERR_WORKSPACE = -3,   /* ws_bytes below the required size */
-  TREE_ATTN_ERR_HIP = -4          /* a HIP launch or runtime call failed */
+  TREE_ATTN_ERR_HIP = -4,         /* a HIP launch or runtime call failed */
+  TREE_ATTN_ERR_SCRATCH = -5      /* tree_attn_replay_fwd_noalloc: the problem needs more
+                                     than TREE_ATTN_STATIC_SCRATCH_BYTES of scratch */
 } tree_attn_status;
 
 typedef enum {
@@ -150,6 +155,38 @@ int tree_attn_prefill(const tree_attn_problem* problem, const void* q_p, const v
 int tree_attn_replay_fwd(const tree_attn_problem* problem, const void* k_p, const void* v_p,
                          const void* q_r, const void* k_r, const void* v_r, void* o_r,
                          float* lse_r, void* ws, size_t ws_bytes, tree_attn_stream_t stream);
+
+/*
+ * Size of the library's static scratch array (one per GPU), used only by
+ * tree_attn_replay_fwd_noalloc: 128 MiB.
+ */
+#define TREE_ATTN_STATIC_SCRATCH_BYTES (128u << 20)
+
+/*
+ * tree_attn_replay_fwd without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Arguments, layout and results are those
+ * of tree_attn_replay_fwd (same kernels, bit-identical outputs); the caller
+ * still provides every input and output tensor.
+ * Scratch.  The work lists, transposed V copies and (for long prompts)
+ * prompt-column partials go to a static device array of
+ * TREE_ATTN_STATIC_SCRATCH_BYTES, one per GPU, allocated with the library's
+ * code object on that GPU and held until the process ends.  The call itself
+ * allocates nothing and frees nothing.  A problem whose scratch would not fit
+ * (tree_attn_workspace_size(problem, TREE_ATTN_OP_REPLAY_FWD, ...) reports the
+ * same size) returns TREE_ATTN_ERR_SCRATCH before any HIP call.
+ * Sharing.  Every call on one GPU uses that GPU's array, and nothing in it
+ * is kept from one call to the next.  Calls whose work overlaps on one GPU
+ * (different streams or host threads without ordering) race on the array
+ * and give undefined results: order them on one stream or synchronise.
+ * Device.  `stream` must belong to the calling thread's current device
+ * (else TREE_ATTN_ERR_INVALID).  The array's device address is looked up
+ * once per device, on the first call made on it.
+ */
+int tree_attn_replay_fwd_noalloc(const tree_attn_problem* problem, const void* k_p,
+                                 const void* v_p, const void* q_r, const void* k_r,
+                                 const void* v_r, void* o_r, float* lse_r,
+                                 tree_attn_stream_t stream);
 
 /*
  * Response replay backward (section 3.2, Eq. 2).  Given the replay forward's

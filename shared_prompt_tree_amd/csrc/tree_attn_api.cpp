@@ -16,6 +16,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "tree_attn.h"
@@ -27,6 +28,7 @@ using namespace treeattn;
 namespace {
 
 constexpr size_t kAlign = 256;
+constexpr size_t kStaticScratchBytes = TREE_ATTN_STATIC_SCRATCH_BYTES;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 long long pad_len(long long n) { return ceil_div(n, kPad) * kPad; }
@@ -407,6 +409,112 @@ FwdShape fwd_shape(const Shape& s, long long items, long long wide_items) {
   return {8, s.tile_q, items};
 }
 
+// Host checks of a replay forward call (problem, tensors); fills s.
+int check_replay_fwd(const tree_attn_problem* problem, const void* k_p, const void* v_p,
+                     const void* q_r, const void* k_r, const void* v_r, void* o_r, float* lse_r,
+                     Shape& s) {
+  const int rc = validate_problem(problem, true, s);
+  if (rc != TREE_ATTN_OK) return rc;
+  if (!tensor_ok(k_p, s.p_tokens) || !tensor_ok(v_p, s.p_tokens)) return TREE_ATTN_ERR_INVALID;
+  for (const void* t : {q_r, k_r, v_r, static_cast<const void*>(o_r), static_cast<const void*>(lse_r)})
+    if (!tensor_ok(t, s.r_tokens)) return TREE_ATTN_ERR_INVALID;
+  return TREE_ATTN_OK;
+}
+
+// The replay forward's launches, with scratch laid out by pl.
+int run_replay_fwd(const tree_attn_problem* problem, const Shape& s, const Plan& pl,
+                   const void* k_p, const void* v_p, const void* q_r, const void* k_r,
+                   const void* v_r, void* o_r, float* lse_r, hipStream_t st) {
+  if (s.r_tokens == 0) return TREE_ATTN_OK;
+  (void)hipGetLastError();
+  const bool split = s.col_splits > 1;
+  const FwdShape fs = split ? FwdShape{8, s.tile_q, s.q_items_replay * s.col_splits}
+                            : fwd_shape(s, s.q_items_replay, s.wq_items_replay);
+  TA_TRY(run_meta(problem, s, pl.mq, kMetaQReplay, s.q_items_replay * s.col_splits, st,
+                  fs.tile_q));
+  TA_TRY(run_transpose(v_p, pl.vt_p, s.hkv, 1, s, s.ng, problem->prompt_cu_d, pl.mq.prompt_pad,
+                       s.p_pad, st));
+  TA_TRY(run_transpose(v_r, pl.vt_r, s.hkv, 1, s, s.nb, problem->resp_cu_d, pl.mq.resp_pad,
+                       s.r_pad, st));
+  FwdLaunch f;
+  f.waves = fs.waves;
+  f.q = q_r;
+  f.o = o_r;
+  f.lse = lse_r;
+  f.k_a = k_p;
+  f.vt_a = pl.vt_p;
+  f.k_b = k_r;
+  f.vt_b = pl.vt_r;
+  f.items = pl.mq.items;
+  f.n_items = (int)fs.items;
+  f.hq = s.hq;
+  f.hkv = s.hkv;
+  f.hp = s.hp;
+  f.d = s.d;
+  f.dtype = s.dtype;
+  f.lse_stride = (int)s.r_tokens;
+  f.vt_a_stride = (int)s.p_pad;
+  f.vt_b_stride = (int)s.r_pad;
+  f.scale = problem->softmax_scale;
+  f.o_part = pl.o_part;
+  f.lse_part = pl.lse_part;
+  TA_TRY(launch_fwd(f, st));
+  if (split)  // the chunks' partial states, merged (section 3.3)
+    TA_TRY(launch_lse_merge(s.col_splits, (int)s.r_tokens, s.hq, s.d, s.dtype, pl.o_part,
+                            pl.lse_part, o_r, lse_r, st));
+  return TREE_ATTN_OK;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------ static scratch
+//
+// Scratch of tree_attn_replay_fwd_noalloc, for callers that cannot allocate
+// device memory: one array per GPU, allocated with the code object when the
+// library is loaded on that device and held until the process ends.  On the
+// host the name `scratch` stands for the variable, not for its device
+// address: host code only ever uses the address looked up below, once per
+// device, with that device current.
+// The array has external linkage: a `static` device array becomes a local
+// symbol of the code object, which the HIP runtime cannot resolve from the
+// host-side variable (it aborts the process instead of returning an error).
+// kAlign bytes of slack let the looked-up address be rounded up to kAlign
+// whatever alignment the code object gives the symbol.
+namespace treeattn {
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes + kAlign];
+}  // namespace treeattn
+
+namespace {
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mutex;
+void* g_scratch_base[kMaxDevices] = {};
+
+// Device address of the scratch array on the device of `stream`, which must
+// be the calling thread's current device.
+int static_scratch(hipStream_t stream, void** base) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (stream != nullptr) {
+    int sdev = -1;
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess) return hip_status(e);
+    if (sdev != dev) return TREE_ATTN_ERR_INVALID;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return TREE_ATTN_ERR_INVALID;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_base[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(treeattn::scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (p == nullptr) return TREE_ATTN_ERR_HIP;
+    g_scratch_base[dev] = reinterpret_cast<void*>(align_up(reinterpret_cast<uintptr_t>(p)));
+  }
+  *base = g_scratch_base[dev];
+  return TREE_ATTN_OK;
+}
+
 }  // namespace
 
 namespace treeattn {
@@ -476,53 +584,30 @@ int tree_attn_replay_fwd(const tree_attn_problem* problem, const void* k_p, cons
                          const void* q_r, const void* k_r, const void* v_r, void* o_r,
                          float* lse_r, void* ws, size_t ws_bytes, tree_attn_stream_t stream) {
   Shape s;
-  int rc = validate_problem(problem, true, s);
+  int rc = check_replay_fwd(problem, k_p, v_p, q_r, k_r, v_r, o_r, lse_r, s);
   if (rc != TREE_ATTN_OK) return rc;
-  if (!tensor_ok(k_p, s.p_tokens) || !tensor_ok(v_p, s.p_tokens)) return TREE_ATTN_ERR_INVALID;
-  for (const void* t : {q_r, k_r, v_r, static_cast<const void*>(o_r), static_cast<const void*>(lse_r)})
-    if (!tensor_ok(t, s.r_tokens)) return TREE_ATTN_ERR_INVALID;
   Plan pl;
   rc = check_ws(s, TREE_ATTN_OP_REPLAY_FWD, ws, ws_bytes, pl);
   if (rc != TREE_ATTN_OK) return rc;
-  if (s.r_tokens == 0) return TREE_ATTN_OK;
+  return run_replay_fwd(problem, s, pl, k_p, v_p, q_r, k_r, v_r, o_r, lse_r,
+                        static_cast<hipStream_t>(stream));
+}
+
+int tree_attn_replay_fwd_noalloc(const tree_attn_problem* problem, const void* k_p,
+                                 const void* v_p, const void* q_r, const void* k_r,
+                                 const void* v_r, void* o_r, float* lse_r,
+                                 tree_attn_stream_t stream) {
+  Shape s;
+  int rc = check_replay_fwd(problem, k_p, v_p, q_r, k_r, v_r, o_r, lse_r, s);
+  if (rc != TREE_ATTN_OK) return rc;
+  if (make_plan(s, TREE_ATTN_OP_REPLAY_FWD, nullptr).bytes > kStaticScratchBytes)
+    return TREE_ATTN_ERR_SCRATCH;  // rejected before any HIP call
   hipStream_t st = static_cast<hipStream_t>(stream);
-  (void)hipGetLastError();
-  const bool split = s.col_splits > 1;
-  const FwdShape fs = split ? FwdShape{8, s.tile_q, s.q_items_replay * s.col_splits}
-                            : fwd_shape(s, s.q_items_replay, s.wq_items_replay);
-  TA_TRY(run_meta(problem, s, pl.mq, kMetaQReplay, s.q_items_replay * s.col_splits, st,
-                  fs.tile_q));
-  TA_TRY(run_transpose(v_p, pl.vt_p, s.hkv, 1, s, s.ng, problem->prompt_cu_d, pl.mq.prompt_pad,
-                       s.p_pad, st));
-  TA_TRY(run_transpose(v_r, pl.vt_r, s.hkv, 1, s, s.nb, problem->resp_cu_d, pl.mq.resp_pad,
-                       s.r_pad, st));
-  FwdLaunch f;
-  f.waves = fs.waves;
-  f.q = q_r;
-  f.o = o_r;
-  f.lse = lse_r;
-  f.k_a = k_p;
-  f.vt_a = pl.vt_p;
-  f.k_b = k_r;
-  f.vt_b = pl.vt_r;
-  f.items = pl.mq.items;
-  f.n_items = (int)fs.items;
-  f.hq = s.hq;
-  f.hkv = s.hkv;
-  f.hp = s.hp;
-  f.d = s.d;
-  f.dtype = s.dtype;
-  f.lse_stride = (int)s.r_tokens;
-  f.vt_a_stride = (int)s.p_pad;
-  f.vt_b_stride = (int)s.r_pad;
-  f.scale = problem->softmax_scale;
-  f.o_part = pl.o_part;
-  f.lse_part = pl.lse_part;
-  TA_TRY(launch_fwd(f, st));
-  if (split)  // the chunks' partial states, merged (section 3.3)
-    TA_TRY(launch_lse_merge(s.col_splits, (int)s.r_tokens, s.hq, s.d, s.dtype, pl.o_part,
-                            pl.lse_part, o_r, lse_r, st));
-  return TREE_ATTN_OK;
+  void* base = nullptr;
+  rc = static_scratch(st, &base);
+  if (rc != TREE_ATTN_OK) return rc;
+  const Plan pl = make_plan(s, TREE_ATTN_OP_REPLAY_FWD, base);
+  return run_replay_fwd(problem, s, pl, k_p, v_p, q_r, k_r, v_r, o_r, lse_r, st);
 }
 
 int tree_attn_replay_bwd(const tree_attn_problem* problem, const void* k_p, const void* v_p,
@@ -758,6 +843,9 @@ const char* tree_attn_error_string(int code) {
     case TREE_ATTN_ERR_UNSUPPORTED: return "unsupported dtype or head_dim";
     case TREE_ATTN_ERR_WORKSPACE: return "workspace too small";
     case TREE_ATTN_ERR_HIP: return "HIP launch or runtime error";
+    case TREE_ATTN_ERR_SCRATCH:
+      return "problem needs more scratch than the static scratch of "
+             "tree_attn_replay_fwd_noalloc (TREE_ATTN_STATIC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

@@ -63,6 +63,7 @@ def library():
     lib.tree_attn_workspace_size.argtypes = [P, ctypes.c_int, ctypes.POINTER(sz)]
     lib.tree_attn_prefill.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.tree_attn_replay_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.tree_attn_replay_fwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.tree_attn_replay_bwd.argtypes = [P] + [vp] * 14 + [sz, vp]
     lib.tree_attn_prefill_bwd.argtypes = [P] + [vp] * 12 + [sz, vp]
     lib.lse_merge.argtypes = [ctypes.c_int32] * 5 + [vp] * 4 + [vp]
@@ -71,6 +72,7 @@ def library():
     lib.tree_attn_last_hip_error.argtypes = []
     lib.tree_attn_set_kernel_events.argtypes = [ctypes.c_int, vp, vp]
     for name in ("tree_attn_workspace_size", "tree_attn_prefill", "tree_attn_replay_fwd",
+                 "tree_attn_replay_fwd_noalloc",
                  "tree_attn_replay_bwd", "tree_attn_prefill_bwd", "lse_merge",
                  "tree_attn_last_hip_error", "tree_attn_set_kernel_events"):
         getattr(lib, name).restype = ctypes.c_int
@@ -257,6 +259,20 @@ def tree_attn_replay_fwd(problem, k_p, v_p, q_r, k_r, v_r, o_r=None, lse_r=None,
         ctypes.byref(problem.c), _ptr(k_p), _ptr(v_p), _ptr(q_r), _ptr(k_r), _ptr(v_r),
         _ptr(o_r), _ptr(lse_r), _ptr(ws), n, _stream(stream)))
     _used_on(stream, ws, *made)
+    return o_r, lse_r
+
+
+STATIC_SCRATCH_BYTES = 128 << 20
+
+
+def tree_attn_replay_fwd_noalloc(problem, k_p, v_p, q_r, k_r, v_r, o_r, lse_r, stream=None):
+    """Response replay forward into caller-provided o_r / lse_r, with the
+    library's static scratch instead of a workspace: no device memory is
+    allocated here or in the library.  Returns (o_r, lse_r)."""
+    _check_tensors(problem, k_p=k_p, v_p=v_p, q_r=q_r, k_r=k_r, v_r=v_r, o_r=o_r, lse_r=lse_r)
+    _check("tree_attn_replay_fwd_noalloc", library().tree_attn_replay_fwd_noalloc(
+        ctypes.byref(problem.c), _ptr(k_p), _ptr(v_p), _ptr(q_r), _ptr(k_r), _ptr(v_r),
+        _ptr(o_r), _ptr(lse_r), _stream(stream)))
     return o_r, lse_r
 
 

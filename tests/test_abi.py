@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol():
 
 def test_error_strings():
     lib = ops.library()
-    for code in (0, -1, -2, -3, -4, 7):
+    for code in (0, -1, -2, -3, -4, -5, 7):
         assert lib.tree_attn_error_string(code)
 
 
@@ -242,6 +242,30 @@ def test_entry_points_reject_before_any_hip_call():
     assert lib.lse_merge(2, 4, 2, 128, 5, fake, fake, fake, fake, None) == -2
     assert lib.lse_merge(2, 4, 2, 128, 1, None, fake, fake, fake, None) == -1
     assert lib.lse_merge(2, 0, 2, 128, 1, None, None, None, None, None) == 0
+
+
+def test_noalloc_replay_rejects_problems_beyond_the_static_scratch():
+    """tree_attn_replay_fwd_noalloc refuses, on the host and before any HIP
+    call, a problem whose replay scratch (the size tree_attn_workspace_size
+    reports) exceeds TREE_ATTN_STATIC_SCRATCH_BYTES, and invalid arguments as
+    the workspace form does."""
+    lib = ops.library()
+    vp = ctypes.c_void_p
+    fake = vp(1 << 20)  # never dereferenced: the call fails first
+    # response-heavy-sized replay: ~2.7 GB of transposed V copies
+    big = small_problem(prompt_cu=[0, 256], group_branch_cu=[0, 256],
+                        resp_cu=np.arange(257) * 5000, num_q_heads=32, num_kv_heads=8)
+    assert ops.tree_attn_workspace_size(big, ops.OP_REPLAY_FWD) > ops.STATIC_SCRATCH_BYTES
+    big.c.prompt_cu_d = big.c.group_branch_cu_d = big.c.resp_cu_d = 1 << 20
+    assert lib.tree_attn_replay_fwd_noalloc(ctypes.byref(big.c), *([fake] * 7), None) == -5
+    assert b"static scratch" in lib.tree_attn_error_string(-5)
+    p = small_problem()
+    assert ops.tree_attn_workspace_size(p, ops.OP_REPLAY_FWD) <= ops.STATIC_SCRATCH_BYTES
+    # no device offsets, then a null tensor
+    assert lib.tree_attn_replay_fwd_noalloc(ctypes.byref(p.c), *([fake] * 7), None) == -1
+    p.c.prompt_cu_d = p.c.group_branch_cu_d = p.c.resp_cu_d = 1 << 20
+    assert lib.tree_attn_replay_fwd_noalloc(ctypes.byref(p.c), fake, fake, None, fake, fake,
+                                            fake, fake, None) == -1
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
