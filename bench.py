@@ -40,8 +40,14 @@ HBM_GBPS = 8000.0
 
 # Algorithmic FLOPs per valid pair and query head, per head_dim, of each
 # main kernel: forward S and PV; dQ kernel recomputes S and dP and forms dQ;
-# dK/dV kernel recomputes S and dP and forms dV and dK.
+# dK/dV kernel recomputes S and dP and forms dV and dK.  With the fused dQ
+# strategy the dK/dV kernel also forms dQ (10) and no dQ kernel runs.
 KERNEL_FLOPS_PER_PAIR_DIM = {"fwd": 4, "dq": 6, "dkv": 8}
+FUSED_FLOPS_PER_PAIR_DIM = {"fwd": 4, "dq": 0, "dkv": 10}
+
+
+def flops_per_pair_dim(kind, fused):
+    return (FUSED_FLOPS_PER_PAIR_DIM if fused else KERNEL_FLOPS_PER_PAIR_DIM)[kind]
 
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -120,7 +126,7 @@ LAUNCH_CALLS = {"fwd": ("prefill", "replay_fwd"), "dq": ("replay_bwd", "prefill_
                 "dkv": ("replay_bwd", "prefill_bwd")}
 
 
-def algorithmic_bytes(tree, kind, call):
+def algorithmic_bytes(tree, kind, call, fused=False):
     """Least HBM traffic of one launch: every operand read once and every
     result written once (the pre-transposed copies and work lists the
     kernels also read are not counted).
@@ -132,7 +138,8 @@ def algorithmic_bytes(tree, kind, call):
                       in; dK_R, dV_R (I/O dtype) and the float32 prompt seeds
                       out
       dkv prefill_bwd Q_P, dO_P, LSE_P, D_P, K_P, V_P and the float32 seeds
-                      in; dK_P, dV_P out"""
+                      in; dK_P, dV_P out
+      (fused dQ strategy: the dK/dV launch also writes dQ of its rows once)"""
     esz = 4 if tree.dtype == "f32" else 2
     hq, hkv, d = tree.hq, tree.hkv, tree.d
     tp, tr = tree.prompt_tokens, tree.resp_tokens
@@ -146,13 +153,15 @@ def algorithmic_bytes(tree, kind, call):
     if kind == "dq":
         keys = tp if call == "prefill_bwd" else tp + tr
         return 2 * q_rows(rows) + 2 * rows * hq * 4 + 2 * kv_rows(keys) + q_rows(rows)
+    dq_out = q_rows(rows) if fused else 0
     if call == "replay_bwd":
         return (2 * q_rows(tr) + 2 * tr * hq * 4 + 2 * kv_rows(tp + tr) + 2 * kv_rows(tr)
-                + 2 * seeds)
-    return 2 * q_rows(tp) + 2 * tp * hq * 4 + 2 * kv_rows(tp) + 2 * seeds + 2 * kv_rows(tp)
+                + 2 * seeds + dq_out)
+    return (2 * q_rows(tp) + 2 * tp * hq * 4 + 2 * kv_rows(tp) + 2 * seeds + 2 * kv_rows(tp)
+            + dq_out)
 
 
-def launch_report(tree, kind, ms, stored):
+def launch_report(tree, kind, ms, stored, fused=(False, False)):
     """Per launch of the dominant kernel in one step: its own duration and
     FLOP rate, its measured HBM bytes (rocprofv3 counters of the stored
     profile, null without one), the algorithmic bytes and the achieved HBM
@@ -165,8 +174,9 @@ def launch_report(tree, kind, ms, stored):
              "replay_bwd": pc["replay_prompt"] + pc["replay_own"]}
     out = []
     for c, call in enumerate(LAUNCH_CALLS[kind]):
-        flops = pairs[call] * tree.hq * tree.d * KERNEL_FLOPS_PER_PAIR_DIM[kind]
-        alg = algorithmic_bytes(tree, kind, call)
+        fz = kind != "fwd" and fused[c]
+        flops = pairs[call] * tree.hq * tree.d * flops_per_pair_dim(kind, fz)
+        alg = algorithmic_bytes(tree, kind, call, fz)
         rec = {"call": call, "ms": round(ms[c], 4),
                "tflops": round(flops / (ms[c] * 1e-3) / 1e12, 2) if ms[c] > 0 else None,
                "algorithmic_bytes": int(alg), "hbm_bytes": None, "hbm_gbps": None,
@@ -199,6 +209,12 @@ def parse():
                         "(kernel-trace stats, FETCH_SIZE and WRITE_SIZE passes) and exit")
     p.add_argument("--summarize-command", default="",
                    help="the profiling command recorded in the summaries")
+    p.add_argument("--dq-strategy", choices=["auto", "separate", "fused"], default="auto",
+                   help="how the backward forms dQ (auto: the library's cost model)")
+    p.add_argument("--dq-ab", action="store_true",
+                   help="instead of the benchmark: time the two backward calls with each dQ "
+                        "strategy, alternating, on each workload of --workload and --also, "
+                        "and print one JSON line")
     p.add_argument("--copy-calibration-mib", type=int, default=1024,
                    help="size of a plain device copy run after the timed region, used to "
                         "scale HBM byte counters in profiling runs (0 to skip)")
@@ -216,7 +232,11 @@ def fail(msg):
     sys.exit(2)
 
 
-def measure_workload(name, steps, warmup, flattened=True, fms_hint=None):
+DQ_STRATEGY_CODES = {"auto": 0, "separate": 1, "fused": 2}
+DQ_STRATEGY_NAMES = {1: "separate", 2: "fused"}
+
+
+def measure_workload(name, steps, warmup, flattened=True, fms_hint=None, dq_strategy="auto"):
     import torch
 
     from shared_prompt_tree_amd import ops
@@ -226,7 +246,13 @@ def measure_workload(name, steps, warmup, flattened=True, fms_hint=None):
     tree = wl.make_tree(spec)
     dev = torch.device("cuda:0")
     t = wl.make_tensors(tree, spec.seed, device=dev, value_scale=spec.value_scale)
-    prob = ops.TreeProblem.from_tree(tree, device=dev)
+    prob = ops.TreeProblem.from_tree(tree, device=dev,
+                                     dq_strategy=DQ_STRATEGY_CODES[dq_strategy])
+    # the strategy each backward call uses (the cost model's choice for auto)
+    used = {call: ops.tree_attn_dq_strategy_of(prob, op)
+            for call, op in (("replay_bwd", ops.OP_REPLAY_BWD),
+                             ("prefill_bwd", ops.OP_PREFILL_BWD))}
+    fused = tuple(used[c] == ops.DQ_FUSED for c in ("replay_bwd", "prefill_bwd"))
     torch.cuda.synchronize()
 
     def step():
@@ -308,21 +334,31 @@ def measure_workload(name, steps, warmup, flattened=True, fms_hint=None):
         "breakdown_ms": {k: round(v, 4) for k, v in part.items()},
         "kernel_ms": {k: round(v, 4) for k, v in kern.items()},
     }
-    # algorithmic FLOPs of each kernel kind over one step
-    kflops = {k: pairs["tree"] * hq * d * f for k, f in KERNEL_FLOPS_PER_PAIR_DIM.items()}
+    # algorithmic FLOPs of each kernel kind over one step (the dQ and dK/dV
+    # kernels per backward call, by the dQ strategy it used)
+    call_pairs = {"prefill": pairs["prefill"],
+                  "replay": pairs["replay_prompt"] + pairs["replay_own"]}
+    kflops = {"fwd": pairs["tree"] * hq * d * 4}
+    for k in ("dq", "dkv"):
+        kflops[k] = sum(call_pairs[c] * hq * d * flops_per_pair_dim(k, fz)
+                        for c, fz in (("replay", fused[0]), ("prefill", fused[1])))
     dom = max(kern, key=kern.get)
     achieved = kflops[dom] / (kern[dom] * 1e-3) / 1e12
     stored = stored_launch_traffic(dom, name)
+    fpd = sorted({flops_per_pair_dim(dom, fz) for fz in fused})
+    rep["dq_strategy"] = {c: DQ_STRATEGY_NAMES[v] for c, v in used.items()}
     rep["roofline"] = {
         "kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
         "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
         "traffic": None if stored is None else round(sum(r + w for r, w in stored) / len(stored)),
-        "flops_per_pair_per_dim": KERNEL_FLOPS_PER_PAIR_DIM[dom],
+        "flops_per_pair_per_dim": fpd[0] if len(fpd) == 1 else fpd,
         "launches_per_step": 2, "ms_per_step": round(kern[dom], 4),
-        "launches": launch_report(tree, dom, [kern_launch[(dom, c)] for c in range(2)], stored),
+        "launches": launch_report(tree, dom, [kern_launch[(dom, c)] for c in range(2)], stored,
+                                  fused),
     }
-    rep["kernel_tflops"] = {k: round(kflops[k] / (kern[k] * 1e-3) / 1e12, 2) for k in kern}
+    rep["kernel_tflops"] = {k: round(kflops[k] / (kern[k] * 1e-3) / 1e12, 2) if kern[k] > 0
+                            else None for k in kern}
     # forward (prefill + replay_fwd) and backward (replay_bwd + prefill_bwd)
     # on their own useful FLOPs (4d and 10d per pair), and the whole step
     # with 12d per pair (no recompute counted) beside the 14d convention
@@ -373,6 +409,93 @@ def measure_workload(name, steps, warmup, flattened=True, fms_hint=None):
     rep["_tree"] = tree
     rep["_tensors"] = t
     return rep
+
+
+def dq_strategy_ab(names, steps):
+    """Same-box A/B of the dQ strategies: on each workload, the replay and
+    prefill backward calls timed with HIP events, the separate pass and the
+    fused kernel alternating (two rounds each, ``steps`` calls per round, the
+    per-strategy figure is the mean of its rounds).  Useful backward TFLOP/s
+    count 10d per valid pair and query head.  The float32 dQ atomic bytes of
+    the fused kernel (d floats per query row and key tile it reads) are
+    reported with the rate they were added at."""
+    import torch
+
+    from shared_prompt_tree_amd import ops
+    from shared_prompt_tree_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    out = {"metric": "dQ strategy A/B: backward call times", "unit": "ms", "rounds": 2,
+           "steps": steps, "workloads": []}
+    for name in names:
+        spec = wl.SPECS[name]
+        tree = wl.make_tree(spec)
+        t = wl.make_tensors(tree, spec.seed, device=dev, value_scale=spec.value_scale)
+        prob = ops.TreeProblem.from_tree(tree, device=dev)
+        o_p, lse_p = ops.tree_attn_prefill(prob, t["q_p"], t["k_p"], t["v_p"])
+        o_r, lse_r = ops.tree_attn_replay_fwd(prob, t["k_p"], t["v_p"], t["q_r"], t["k_r"],
+                                              t["v_r"])
+        pc = wl.pair_counts(tree)
+        useful = {"replay_bwd": (pc["replay_prompt"] + pc["replay_own"]) * tree.hq * tree.d * 10,
+                  "prefill_bwd": pc["prefill"] * tree.hq * tree.d * 10}
+        visits = {"replay_bwd": 0, "prefill_bwd": 0}
+        for P, rs in zip(tree.prompt_lens, tree.resp_lens):
+            visits["prefill_bwd"] += causal_tile_visits(P)
+            for r in rs:
+                visits["replay_bwd"] += r * (-(-P // 256)) + causal_tile_visits(r)
+        times = {st: {"replay_bwd": [], "prefill_bwd": []} for st in ("separate", "fused")}
+        for _ in range(2):
+            for st in ("separate", "fused"):
+                prob.dq_strategy = DQ_STRATEGY_CODES[st]
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                res = ops.tree_attn_replay_bwd(prob, t["k_p"], t["v_p"], t["q_r"], t["k_r"],
+                                               t["v_r"], o_r, lse_r, t["do_r"])
+                ops.tree_attn_prefill_bwd(prob, t["q_p"], t["k_p"], t["v_p"], o_p, lse_p,
+                                          t["do_p"], res[3], res[4])
+                torch.cuda.synchronize()
+                tr = tp = 0.0
+                for _ in range(steps):
+                    e[0].record()
+                    res = ops.tree_attn_replay_bwd(prob, t["k_p"], t["v_p"], t["q_r"],
+                                                   t["k_r"], t["v_r"], o_r, lse_r, t["do_r"])
+                    e[1].record()
+                    ops.tree_attn_prefill_bwd(prob, t["q_p"], t["k_p"], t["v_p"], o_p, lse_p,
+                                              t["do_p"], res[3], res[4])
+                    e[2].record()
+                    torch.cuda.synchronize()
+                    tr += e[0].elapsed_time(e[1]) / steps
+                    tp += e[1].elapsed_time(e[2]) / steps
+                times[st]["replay_bwd"].append(tr)
+                times[st]["prefill_bwd"].append(tp)
+                print(f"[ab] {name} {st}: replay_bwd {tr:.3f} ms, prefill_bwd {tp:.3f} ms",
+                      file=sys.stderr, flush=True)
+        rec = {"workload": name}
+        for st, calls in times.items():
+            rec[st] = {}
+            for call, ts in calls.items():
+                ms = sum(ts) / len(ts)
+                r = {"ms": round(ms, 4), "rounds_ms": [round(x, 4) for x in ts],
+                     "useful_tflops": round(useful[call] / (ms * 1e-3) / 1e12, 1)}
+                if st == "fused":
+                    ab = visits[call] * tree.hq * tree.d * 4
+                    r["atomic_bytes"] = int(ab)
+                    r["atomic_tbps"] = round(ab / (ms * 1e-3) / 1e12, 3)
+                rec[st][call] = r
+        prob.dq_strategy = 0
+        rec["auto_chooses"] = {c: DQ_STRATEGY_NAMES[ops.tree_attn_dq_strategy_of(prob, op)]
+                               for c, op in (("replay_bwd", ops.OP_REPLAY_BWD),
+                                             ("prefill_bwd", ops.OP_PREFILL_BWD))}
+        out["workloads"].append(rec)
+        del t, o_p, lse_p, o_r, lse_r, res
+        torch.cuda.empty_cache()
+    return out
+
+
+def causal_tile_visits(n, tile=256):
+    """Key tiles read by the rows of an n-token causal segment:
+    sum over k = 1..n of ceil(k / tile)."""
+    m, q = divmod(n, tile)
+    return tile * m * (m + 1) // 2 + q * (m + 1)
 
 
 def cpu_baseline(tree, t, workers):
@@ -539,9 +662,15 @@ def main():
     from shared_prompt_tree_amd import ops
 
     ops.library()  # fail loudly if the HIP library is missing
+    if args.dq_ab:
+        names = [args.workload] + ([] if args.also in ("", "none") else
+                                   [n for n in args.also.split(",") if n != args.workload])
+        print(json.dumps(dq_strategy_ab(names, args.steps)), flush=True)
+        return
     print(f"[bench] workload {args.workload}: warmup {args.warmup}, steps {args.steps}",
           file=sys.stderr, flush=True)
-    main_rep = measure_workload(args.workload, args.steps, args.warmup, not args.no_flattened)
+    main_rep = measure_workload(args.workload, args.steps, args.warmup, not args.no_flattened,
+                                dq_strategy=args.dq_strategy)
     print(f"[bench] {args.workload}: {main_rep['ms_per_step']:.2f} ms/step, "
           f"{main_rep['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
     cpu = None
@@ -561,7 +690,8 @@ def main():
         print(f"[bench] workload {aname}: warmup {a_warm}, steps {a_steps}", file=sys.stderr,
               flush=True)
         a = measure_workload(aname, a_steps, a_warm, not args.no_flattened,
-                             fms_hint=1 if aname in ALSO_STEPS else None)
+                             fms_hint=1 if aname in ALSO_STEPS else None,
+                             dq_strategy=args.dq_strategy)
         a.pop("_tree")
         a.pop("_tensors")
         also.append({
@@ -572,6 +702,7 @@ def main():
             "breakdown_ms": a["breakdown_ms"], "kernel_ms": a["kernel_ms"],
             "kernel_tflops": a["kernel_tflops"], "roofline": a["roofline"],
             "phases": a["phases"], "useful_tflops_12d": a["useful_tflops_12d"],
+            "dq_strategy": a["dq_strategy"],
             "flattened_baseline": a.get("flattened_baseline"), "config": a["config"],
         })
         print(f"[bench] {aname}: {a['ms_per_step']:.2f} ms/step, {a['tflops']:.1f} TFLOP/s",
@@ -610,6 +741,7 @@ def main():
         "kernel_tflops": main_rep["kernel_tflops"],
         "phases": main_rep["phases"],
         "useful_tflops_12d": main_rep["useful_tflops_12d"],
+        "dq_strategy": main_rep["dq_strategy"],
         "roofline": main_rep["roofline"],
         "flattened_baseline": main_rep.get("flattened_baseline"),
         "cpu_baseline": cpu,

@@ -44,8 +44,11 @@
  * 4 GiB.  The packed head count is the largest power of two (at most 16)
  * dividing Hq / Hkv.  Larger problems are rejected with
  * TREE_ATTN_ERR_INVALID.
- * Determinism.  No output is accumulated with atomics: every partial sum
- * is added in a fixed order, so repeated calls give bit-identical results.
+ * Determinism.  With the default dQ strategies no output is accumulated
+ * with atomics: every partial sum is added in a fixed order, so repeated
+ * calls give bit-identical results.  TREE_ATTN_DQ_FUSED (below) adds dQ
+ * with float32 atomics; there dQ varies from call to call by rounding and
+ * every other output stays bit-identical.
  * Errors.  0 on success, else a negative tree_attn_status.  Arguments are
  * checked on the host before any HIP call, so a rejected call enqueues
  * nothing and writes nothing.  TREE_ATTN_ERR_HIP reports a failed launch.
@@ -80,6 +83,25 @@ typedef enum {
                                      than TREE_ATTN_STATIC_SCRATCH_BYTES of scratch */
 } tree_attn_status;
 
+/*
+ * How the two backward calls form dQ (the attention definition of section
+ * 2.2 differentiated; S = scale Q K^T, P = softmax, dS = P (dP - D)):
+ *   TREE_ATTN_DQ_SEPARATE  a query-stationary pass recomputes S and dP and
+ *       forms dQ = scale dS K with no atomics (seven matrix products per
+ *       tile, bit-deterministic);
+ *   TREE_ATTN_DQ_FUSED     the key-stationary dK/dV kernel also forms dQ from
+ *       the dS it holds (five products) and adds it into a float32
+ *       accumulator with atomics; bf16 with head_dim 128 only (else
+ *       TREE_ATTN_ERR_UNSUPPORTED), dQ not bit-deterministic;
+ *   TREE_ATTN_DQ_AUTO      the library picks one per call from a cost model
+ *       (section 3.4, "Cost model", in spirit).
+ */
+typedef enum {
+  TREE_ATTN_DQ_AUTO = 0,
+  TREE_ATTN_DQ_SEPARATE = 1,
+  TREE_ATTN_DQ_FUSED = 2
+} tree_attn_dq_strategy;
+
 typedef enum {
   TREE_ATTN_OP_PREFILL = 0,
   TREE_ATTN_OP_REPLAY_FWD = 1,
@@ -105,6 +127,9 @@ typedef enum {
  * Each offset array is given twice: *_h in host memory, *_d in device
  * memory, with equal contents.  The device copies may be NULL only for an
  * entry point that does not read them (none of the four attention calls).
+ * dq_strategy   a tree_attn_dq_strategy (0, the automatic choice, when the
+ *               struct is zero-initialised); the workspace size depends on
+ *               it, so size and call with the same value.
  */
 typedef struct {
   int32_t num_groups;
@@ -120,6 +145,7 @@ typedef struct {
   const int32_t* group_branch_cu_d;
   const int32_t* resp_cu_h;
   const int32_t* resp_cu_d;
+  int32_t dq_strategy;
 } tree_attn_problem;
 
 /*
@@ -238,6 +264,15 @@ int tree_attn_prefill_bwd(const tree_attn_problem* problem, const void* q_p, con
 int lse_merge(int32_t num_splits, int32_t rows, int32_t heads, int32_t head_dim,
               int32_t out_dtype, const float* o_parts, const float* lse_parts, void* o_out,
               float* lse_out, tree_attn_stream_t stream);
+
+/*
+ * The dQ strategy (TREE_ATTN_DQ_SEPARATE or TREE_ATTN_DQ_FUSED) that entry
+ * point `op` (TREE_ATTN_OP_REPLAY_BWD or TREE_ATTN_OP_PREFILL_BWD) uses for
+ * this problem: problem->dq_strategy when explicit, else the cost model's
+ * choice.  Writes *strategy; no HIP call.  TREE_ATTN_ERR_INVALID for another
+ * op; problem errors as tree_attn_workspace_size.
+ */
+int tree_attn_dq_strategy_of(const tree_attn_problem* problem, int op, int* strategy);
 
 /* A static description of a tree_attn_status code. */
 const char* tree_attn_error_string(int code);

@@ -261,12 +261,40 @@ struct DkvArgs {
   float* dv_seed;
   float* part_k;
   float* part_v;
+  float* dq_acc;  // fused variant: float32 dQ / scale accumulated by atomics [tokens][hq][D]
   const KItem* items;
   int n_items;
   int hq, hkv, hp, nsub;
   int lse_stride, qt_stride;
   float scale_log2, scale;
 };
+
+// Fused variant: the resident K tile is stored without padding, 16 chunks
+// per key, chunk c of key r at position c ^ kswz(r).  Sixteen consecutive
+// keys read at one chunk (the score phase) land on sixteen different chunk
+// positions, and so do the 4 keys x 2 chunks of one transposing read group
+// (the dQ phase): no bank conflicts, and the 4 KB of padding are free for
+// the dS exchange buffer.
+__device__ __forceinline__ int kswz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+
+// Copy ROWS keys x 16 chunks into the swizzled layout (global_load_lds, as
+// g2l_tile; LDS chunk p holds chunk (p % 16) ^ kswz(p / 16) of key p / 16).
+template <typename T, int ROWS, int NT, typename RowOff>
+__device__ __forceinline__ void g2l_tile_swz(T* tile, const T* base, RowOff row_off) {
+  constexpr int CH = 16 / sizeof(T), NCH = 16, NCHUNK = ROWS * NCH;
+  static_assert(NCHUNK % NT == 0, "whole wave copies");
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint32_t tile_lds = (uint32_t)(uintptr_t)tile;
+#pragma unroll
+  for (int i = 0; i < NCHUNK / NT; ++i) {
+    const int p0 = i * NT + 64 * w;
+    const int p = p0 + lane;
+    const int q = p / NCH;
+    const int c = (p % NCH) ^ kswz(q);
+    const uint32_t off = ((uint32_t)row_off(q) + (uint32_t)(c * CH)) * (uint32_t)sizeof(T);
+    dma_16(base, off, tile_lds + (uint32_t)p0 * 16u);
+  }
+}
 
 // Key-stationary dK/dV.  A workgroup of NW = 8 waves owns 32 * NW keys of one
 // kv head; wave w owns keys [32w, 32w + 32).  Inside a wave the VALU work
@@ -276,27 +304,44 @@ struct DkvArgs {
 // whole loop (registers would not fit two waves per SIMD), for float32 K
 // stays in registers.  Query blocks of 32 rows (Q, dO, Q^T, dO^T, LSE, D)
 // stream through LDS, double buffered.
-template <typename T, int D>
+//
+// FUSED (bf16, head_dim 128): the same kernel also forms dQ from the dS it
+// already holds, so S and dP are computed once per pair (five products
+// instead of seven).  Each wave writes its dS^T block to an LDS buffer; after
+// a barrier, four waves (one per SIMD, alternating halves of the workgroup
+// from block to block) each multiply dS [32 rows x 256 keys] by K [256 keys
+// x 32 columns of d], reading K^T fragments with transposing LDS reads from
+// the resident K tile, and add the result to a float32 dQ accumulator with
+// atomics (summed over key tiles in no fixed order: dQ is not bit-identical
+// from run to run).
+template <typename T, int D, bool FUSED = false>
 __global__ __launch_bounds__(512) void dkv_kernel(DkvArgs<T, D> a) {
   constexpr int NW = 8, NT = 64 * NW, QB = 32, CH = ChunkOf<T>::kElems;
+  static_assert(!FUSED || (sizeof(T) == 2 && D == 128), "fused variant: bf16, head_dim 128");
   constexpr bool KLDS = sizeof(T) == 2;
   constexpr int NCHQ = D / CH, NCHT = QB / CH;
   constexpr int QROW = tile_row_elems<T, NCHQ>(), TROW = tile_row_elems<T, NCHT>();
   constexpr int QTILE = tile_elems<T, QB, NCHQ>();  // Q or dO block
   constexpr int TTILE = tile_elems<T, D, NCHT>();   // Q^T or dO^T block
   constexpr int STAGE = 2 * QTILE + 2 * TTILE;      // Q, dO, Q^T, dO^T
-  constexpr int KTILE = KLDS ? tile_elems<T, 32 * NW, NCHQ>() : 0;  // resident K tile
+  // resident K tile (padded rows; the fused variant swizzled, unpadded)
+  constexpr int KTILE = !KLDS ? 0 : FUSED ? 32 * NW * D : tile_elems<T, 32 * NW, NCHQ>();
   constexpr int NKK = D / 16, NDB = D / 32;
+  constexpr int DSROW = 32 * NW + CH;  // fused: dS buffer row, 256 keys + one padding chunk
   extern __shared__ __align__(16) unsigned char smem_raw[];
   T* smem = reinterpret_cast<T*>(smem_raw);
   T* ktile = smem + 2 * STAGE;
   float* fsm = reinterpret_cast<float*>(ktile + KTILE);  // [2][2][QB] lse2, delta
+  T* dsb = reinterpret_cast<T*>(fsm + 4 * QB);           // fused: dS [QB rows][DSROW]
 
   int item_idx, kv;
   if (!xcd_map(blockIdx.x, a.n_items, a.hkv, item_idx, kv)) return;
   const KItem it = a.items[item_idx];
   if (it.nk <= 0) return;
-  if ((it.kind == 1 || it.kind == 3) && a.dk_seed == nullptr) return;  // detached prompt
+  // Detached prompt: no seeds to form.  (The fused variant still walks the
+  // prompt tiles: their dS feeds dQ of the response rows.)
+  const bool no_seeds = (it.kind == 1 || it.kind == 3) && a.dk_seed == nullptr;
+  if (!FUSED && no_seeds) return;
   const T* ksrc = it.kind == 0 ? a.k : a.k_prompt;
   const T* vsrc = it.kind == 0 ? a.v : a.v_prompt;
 
@@ -326,7 +371,9 @@ __global__ __launch_bounds__(512) void dkv_kernel(DkvArgs<T, D> a) {
   if constexpr (KLDS) {
     // resident K tile [32*NW keys][D]; keys past the tile end are clamped
     const T* kb = ksrc + (size_t)it.k0 * kv_stride + kv * D;
-    g2l_tile<T, 32 * NW, NCHQ, NT>(ktile, kb, [&](int r) { return min(r, it.nk - 1) * (int)kv_stride; });
+    auto kro = [&](int r) { return min(r, it.nk - 1) * (int)kv_stride; };
+    if constexpr (FUSED) g2l_tile_swz<T, 32 * NW, NT>(ktile, kb, kro);
+    else g2l_tile<T, 32 * NW, NCHQ, NT>(ktile, kb, kro);
   }
 
   // Query block cursor: head sub-group hs, segment seg, block blk.  Blocks
@@ -411,6 +458,8 @@ __global__ __launch_bounds__(512) void dkv_kernel(DkvArgs<T, D> a) {
   const int wave_kmax = wave_kmin + 31;
   const bool wave_has_keys = 32 * w < it.nk;
   const int krow = 32 * w + lr;               // this lane's row of the K tile
+  const bool key_ok = krow < it.nk;
+  int bpar = 0;  // fused: which half of the workgroup forms dQ for this block
 
   Cur cur{a.nsub - 1, it.seg_hi - 1, 0, 0, 0, 0, 0};
   bool have = false;
@@ -450,7 +499,13 @@ __global__ __launch_bounds__(512) void dkv_kernel(DkvArgs<T, D> a) {
       // S = Q K^T (operand loads one step ahead)
       auto sload = [&](int kk, int slot) {
         lds_frag(fa[slot], qs, lr, QROW, 16 * kk + 8 * lh);
-        if constexpr (KLDS) lds_frag(fb[slot], ktile, krow, QROW, 16 * kk + 8 * lh);
+        if constexpr (FUSED) {
+          int ko = krow;  // recomputed per read, not kept across the loop
+          asm volatile("" : "+v"(ko));
+          load_frag(fb[slot], ktile + ko * D + (((2 * kk + lh) ^ kswz(ko)) << 3));
+        }
+        else if constexpr (KLDS)
+          lds_frag(fb[slot], ktile, krow, QROW, 16 * kk + 8 * lh);
       };
       sload(0, 0);
 #pragma unroll
@@ -535,16 +590,111 @@ __global__ __launch_bounds__(512) void dkv_kernel(DkvArgs<T, D> a) {
           oload(n + 2);
           mma(dka[st >> 1], sf[st & 1], fr[n % 3]);
         }
+        if constexpr (FUSED) {
+          // dS of this wave's keys into the exchange buffer [row][key]
+          // (keys past the tile end are 0: their clamped K rows must add
+          // nothing to dQ)
+#pragma unroll
+          for (int jj = 0; jj < 16; ++jj) {
+            const int r = 8 * (jj >> 2) + 4 * lh + (jj & 3);
+            dsb[r * DSROW + krow] = key_ok ? sf[jj >> 3].v[jj & 7] : static_cast<T>(0.f);
+          }
+        }
       }
     }
-    if (more) lstore(stage ^ 1);
-    wait_vmem();
-    __syncthreads();
+    if constexpr (FUSED) {
+      if (skip) {
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj)
+          dsb[(8 * (jj >> 2) + 4 * lh + (jj & 3)) * DSROW + krow] = static_cast<T>(0.f);
+      }
+      // The next stage's LSE / D row is stored before the atomics below, so
+      // the wait for its global load cannot also wait for them.
+      if (more) lstore(stage ^ 1);
+      // every wave's dS is in LDS before the dQ products read it
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if ((w >> 2) == bpar) {
+        // dQ[32 rows][32 db .. 32 db + 31] += dS[32 rows][256 keys] K[256 keys][...]
+        // A: dS row lr, keys 16 ks + 8 lh .. +7 (16-byte read);
+        // B: K^T, two transposing reads of keys 16 ks + 8 lh + 4 t .. +3 for
+        //    column 32 db + (l % 32) (lane l of a 16-lane group reads key
+        //    key0 + l16 / 4, columns 4 (l16 % 4) .. +3 of its half of the block)
+        // Lane-derived addresses are recomputed here from an opaque copy of
+        // the lane index rather than kept across the block loop (registers
+        // are full there).
+        int lo = l;
+        asm volatile("" : "+v"(lo));
+        const int lro = lo & 31, lho = lo >> 5;
+        const int db = w & 3, l16 = lo & 15, g1 = (lo >> 4) & 1;
+        const int kr0 = 8 * lho + (l16 >> 2);
+        const int dcol = 32 * db + 16 * g1 + 4 * (l16 & 3);
+        const int off0 = kr0 * D + ((((dcol >> 3) ^ kswz(kr0)) << 3) | (dcol & 7));
+        const int off1 = (kr0 + 4) * D + ((((dcol >> 3) ^ kswz(kr0 + 4)) << 3) | (dcol & 7));
+        const T* arow = dsb + lro * DSROW + 8 * lho;
+        f32x16 qacc = f32x16{};
+        Frag<T> qa[2], qb[2];
+        auto dqload = [&](int ks, int slot) {
+          load_frag(qa[slot], arow + 16 * ks);
+          const bf16x4 b0 = lds_read_tr(ktile + 16 * ks * D + off0);
+          const bf16x4 b1 = lds_read_tr(ktile + 16 * ks * D + off1);
+          qb[slot].v = bf16x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+        };
+        // two key steps per iteration, the next pair's operands loaded while
+        // this pair multiplies (a rolled loop keeps the operands in flight
+        // to two pairs: the dK/dV accumulators leave no more registers)
+        constexpr int NKS = (32 * NW) / 16;
+        dqload(0, 0);
+        dqload(1, 1);
+#pragma unroll 1
+        for (int ks = 0; ks < NKS; ks += 2) {
+          mma(qacc, qa[0], qb[0]);
+          if (ks + 2 < NKS) dqload(ks + 2, 0);
+          mma(qacc, qa[1], qb[1]);
+          if (ks + 3 < NKS) dqload(ks + 3, 1);
+        }
+        // qacc: lane l, register jj -> row 8 (jj / 4) + 4 lh + jj % 4, column
+        // 32 db + lr.  Exactly 16 atomics per lane (rows past the segment add
+        // 0 to its last row), so the wait below can leave them in flight.
+        // Row r of the block is token tok0 + r / hp, head hg * hp + r % hp (hp
+        // a power of two); the block's rows span at most 32 tokens of one
+        // segment, so offsets from the block's first row fit in 32 bits.
+        const int tok0 = cur.blk * tpb;
+        const int hg = kv * a.nsub + cur.hs;
+        const int lg = 31 - __builtin_clz(hp);
+        const int tlast = cur.nq - 1 - tok0;  // last token of the segment, block-relative
+        float* qb0 = a.dq_acc + ((size_t)(cur.q0 + tok0) * a.hq + (size_t)hg * hp) * D + 32 * db;
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) {
+          int la = l;
+          asm volatile("" : "+v"(la));
+          const int r = 8 * (jj >> 2) + 4 * (la >> 5) + (jj & 3);
+          const int tk = r >> lg;
+          const bool ok = tk <= tlast;
+          const uint32_t o = (uint32_t)(((ok ? tk : tlast) * a.hq + (r & (hp - 1))) * D + (la & 31));
+          __hip_atomic_fetch_add(qb0 + o, ok ? qacc[jj] : 0.f, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+    if (!FUSED && more) lstore(stage ^ 1);
+    if constexpr (FUSED) {
+      // Vector memory operations complete in issue order: vmcnt(16) leaves
+      // only the 16 atomics just issued in flight, after the tile copies.
+      if ((w >> 2) == bpar)
+        asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      bpar ^= 1;
+    } else {
+      wait_vmem();
+      __syncthreads();
+    }
     cur = nxt;
     stage ^= 1;
     have = more;
   }
 
+  if (no_seeds) return;
   // dka/dva: lane l, register jj -> key 8*(jj/4) + 4*lh + jj%4 of this wave,
   // column 32*db + lr.
 #pragma unroll
@@ -618,7 +768,7 @@ static hipError_t launch_dq_t(const DqLaunch& l, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename T, int D>
+template <typename T, int D, bool FUSED = false>
 static hipError_t launch_dkv_t(const DkvLaunch& l, hipStream_t s) {
   DkvArgs<T, D> a;
   a.k = static_cast<const T*>(l.k);
@@ -649,20 +799,25 @@ static hipError_t launch_dkv_t(const DkvLaunch& l, hipStream_t s) {
   a.qt_stride = l.qt_stride;
   a.scale_log2 = l.scale * kLog2e;
   a.scale = l.scale;
+  a.dq_acc = l.dq_acc;
   constexpr int CH = 16 / sizeof(T);
-  const size_t ktile = sizeof(T) == 2 ? (size_t)tile_elems<T, kTileKV, D / CH>() * sizeof(T) : 0;
+  const size_t ktile = sizeof(T) != 2 ? 0
+                       : FUSED    ? (size_t)kTileKV * D * sizeof(T)
+                                  : (size_t)tile_elems<T, kTileKV, D / CH>() * sizeof(T);
+  const size_t dsbuf = FUSED ? (size_t)32 * (kTileKV + CH) * sizeof(T) : 0;
   const size_t smem =
       2 * sizeof(T) * (size_t)(2 * tile_elems<T, 32, D / CH>() + 2 * tile_elems<T, D, 32 / CH>()) +
-      ktile + 2 * 2 * 32 * sizeof(float);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(dkv_kernel<T, D>),
+      ktile + 2 * 2 * 32 * sizeof(float) + dsbuf;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(dkv_kernel<T, D, FUSED>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
   const int grid = xcd_grid(l.n_items, l.hkv);
   if (grid <= 0) return hipSuccess;
   hipEvent_t e0, e1;
   kernel_events(kKernelDkv, &e0, &e1);
-  if (e0) hipExtLaunchKernelGGL(dkv_kernel<T, D>, dim3(grid), dim3(512), smem, s, e0, e1, 0, a);
-  else dkv_kernel<T, D><<<dim3(grid), dim3(512), smem, s>>>(a);
+  if (e0)
+    hipExtLaunchKernelGGL(dkv_kernel<T, D, FUSED>, dim3(grid), dim3(512), smem, s, e0, e1, 0, a);
+  else dkv_kernel<T, D, FUSED><<<dim3(grid), dim3(512), smem, s>>>(a);
   return hipGetLastError();
 }
 
@@ -672,6 +827,10 @@ hipError_t launch_dq(const DqLaunch& l, hipStream_t s) {
 }
 
 hipError_t launch_dkv(const DkvLaunch& l, hipStream_t s) {
+  if (l.dq_acc != nullptr) {  // fused dK/dV/dQ: bf16, head_dim 128 only (host checked)
+    if (l.dtype != 1 || l.d != 128) return hipErrorInvalidValue;
+    return launch_dkv_t<bf16, 128, true>(l, s);
+  }
   if (l.dtype == 1) return l.d == 128 ? launch_dkv_t<bf16, 128>(l, s) : launch_dkv_t<bf16, 64>(l, s);
   return l.d == 128 ? launch_dkv_t<float, 128>(l, s) : launch_dkv_t<float, 64>(l, s);
 }

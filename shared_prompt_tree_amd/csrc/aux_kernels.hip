@@ -300,26 +300,40 @@ __global__ __launch_bounds__(kAuxThreads) void seed_reduce_kernel(SeedReduceArgs
 // elements.
 template <typename T>
 __global__ __launch_bounds__(kAuxThreads) void sum_parts_kernel(const float* in, int parts,
-                                                                long long n, T* out) {
+                                                                long long n, T* out, float scale) {
   for (long long q = aux_first(blockIdx.x, threadIdx.x); q < n / 4; q += aux_stride(gridDim.x)) {
     const long long i = q * 4;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int k = 0; k < parts; ++k) acc += *reinterpret_cast<const f32x4*>(in + k * n + i);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) out[i + e] = static_cast<T>(acc[e]);
+    for (int e = 0; e < 4; ++e) out[i + e] = static_cast<T>(acc[e] * scale);
   }
 }
 
 hipError_t launch_sum_parts(const float* in, int parts, long long n, void* out, int dtype,
-                            hipStream_t s) {
+                            hipStream_t s, float scale) {
   if (n == 0) return hipSuccess;
   const int grid = (int)aux_blocks(n / 4);
   if (dtype == 1)
     hipLaunchKernelGGL(sum_parts_kernel<bf16>, dim3(grid), dim3(kAuxThreads), 0, s, in, parts, n,
-                       static_cast<bf16*>(out));
+                       static_cast<bf16*>(out), scale);
   else
     hipLaunchKernelGGL(sum_parts_kernel<float>, dim3(grid), dim3(kAuxThreads), 0, s, in, parts, n,
-                       static_cast<float*>(out));
+                       static_cast<float*>(out), scale);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ zero fill
+
+__global__ __launch_bounds__(kAuxThreads) void zero_kernel(float* p, long long n4) {
+  for (long long q = aux_first(blockIdx.x, threadIdx.x); q < n4; q += aux_stride(gridDim.x))
+    *reinterpret_cast<f32x4*>(p + 4 * q) = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+hipError_t launch_zero(float* p, long long n, hipStream_t s) {
+  // n is a multiple of 4 (whole rows of head_dim floats)
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_kernel, dim3((int)aux_blocks(n / 4)), dim3(kAuxThreads), 0, s, p, n / 4);
   return hipGetLastError();
 }
 

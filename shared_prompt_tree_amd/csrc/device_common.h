@@ -144,6 +144,22 @@ __device__ __forceinline__ void g2l_tile(T* tile, const T* base, RowOff row_off)
   }
 }
 
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane j passes the address of 4 consecutive 16-bit elements; lane i
+// receives element i % 4 of the 4-element runs addressed by lanes
+// 4e + i / 4, for e = 0..3.  When lane j addresses row r0 + j / 4, columns
+// c0 + 4 (j % 4) .. +3 of a row-major matrix, lane i therefore receives
+// column c0 + i of rows r0 .. r0 + 3: a 4 x 16 block read column-wise, the
+// layout of an MFMA operand whose contraction runs down the rows.  The
+// address must be 8-byte aligned.
+__device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  lds_v4i16* q = (lds_v4i16*)(const_cast<bf16*>(p));
+  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(q);
+  return __builtin_bit_cast(bf16x4, r);
+}
+
 // Wait until this wave's outstanding memory operations (including the
 // global-to-LDS copies above) have completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }

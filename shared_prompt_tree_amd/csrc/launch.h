@@ -139,10 +139,11 @@ struct DqLaunch {
 };
 hipError_t launch_dq(const DqLaunch& a, hipStream_t s);
 
-// out[i] = sum over k < parts of in[k * n + i], in the output dtype (0 float32,
-// 1 bf16); the chunk partial sums of a split dQ.
+// out[i] = scale * sum over k < parts of in[k * n + i], in the output dtype
+// (0 float32, 1 bf16); the chunk partial sums of a split dQ, or (one part)
+// the scaled float32 dQ accumulator of the fused backward.
 hipError_t launch_sum_parts(const float* in, int parts, long long n, void* out, int dtype,
-                            hipStream_t s);
+                            hipStream_t s, float scale = 1.f);
 
 struct DkvLaunch {
   const void* k;       // own-branch keys (kind 0 tiles) [tokens][hkv][d]
@@ -169,7 +170,15 @@ struct DkvLaunch {
   int lse_stride;
   int qt_stride;       // columns per d row of the transposed copies
   float scale;
+  // Fused variant (bf16, head_dim 128): also adds dQ / scale of the query
+  // rows to this float32 accumulator [tokens][hq][d] (zeroed beforehand),
+  // with atomics.  Null: dK/dV only.
+  float* dq_acc;
 };
 hipError_t launch_dkv(const DkvLaunch& a, hipStream_t s);
+
+// Fill n floats with zero (a kernel, so that captured graphs hold no memset
+// node).
+hipError_t launch_zero(float* p, long long n, hipStream_t s);
 
 }  // namespace treeattn

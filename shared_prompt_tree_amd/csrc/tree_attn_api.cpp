@@ -53,6 +53,8 @@ struct Shape {
   long long own_work = 0;      // own-branch 64-key steps over the replay query tiles
   long long own_max = 0;       // most own-branch steps of one query tile
   long long prompt_work = 0;   // prompt-column 64-key steps over the replay query tiles
+  bool fused_replay = false;   // replay backward forms dQ in the dK/dV kernel
+  bool fused_prefill = false;  // prefill backward likewise
 };
 
 // A replay key-stationary item reading more than the launch's total rows
@@ -108,8 +110,60 @@ int choose_col_splits(const Shape& s) {
   return best;
 }
 
+// dQ strategy of a backward call under TREE_ATTN_DQ_AUTO: a cost model in
+// the spirit of the planner's (section 3.4, "Cost model", Eqs. 7-10: compute
+// plus movement terms with constants calibrated on measured runs), on one
+// GPU.  Per call, with `pairs` the valid (row, key) pairs times Hq:
+//   separate  pairs * 14 d / kSepFlops          (dQ pass 6d + dK/dV 8d)
+//   fused     max(pairs * 10 d / kFusedFlops,   (one pass, 10d)
+//                 atomic bytes / kAtomicBytes)  (dQ added per key tile)
+// where every query row adds d float32 per key tile it reads (its group's
+// prompt tiles plus the causal tiles of its own segment).  The constants
+// come from same-box runs of both strategies on the prompt-heavy,
+// response-heavy and long-mixed workloads: the separate kernels ran at
+// 1.04-1.06 PFLOP/s of executed work, the fused kernel added its dQ rows at
+// 0.79-0.97 TB/s, below the time of its arithmetic, so it is bound by the
+// atomics (2 bytes per pair at head_dim 128) and the model prefers the
+// separate pass on every shape measured.
+constexpr double kSepFlops = 1.05e15;
+constexpr double kFusedFlops = 1.06e15;
+constexpr double kAtomicBytes = 0.95e12;
+
+// sum over k = 1..n of ceil(k / kTileKV): key tiles read by the rows of an
+// n-token causal segment
+double causal_tile_visits(long long n) {
+  const long long m = n / kTileKV, q = n % kTileKV;
+  return (double)kTileKV * m * (m + 1) / 2 + (double)q * (m + 1);
+}
+
+bool choose_dq_fused(const tree_attn_problem* p, const Shape& s, bool replay) {
+  double pairs = 0, visits = 0;
+  for (int g = 0; g < s.ng; ++g) {
+    const long long P = p->prompt_cu_h[g + 1] - p->prompt_cu_h[g];
+    if (!replay) {
+      pairs += (double)P * (P + 1) / 2;
+      visits += causal_tile_visits(P);
+      continue;
+    }
+    for (int i = p->group_branch_cu_h[g]; i < p->group_branch_cu_h[g + 1]; ++i) {
+      const long long r = p->resp_cu_h[i + 1] - p->resp_cu_h[i];
+      pairs += (double)r * P + (double)r * (r + 1) / 2;
+      visits += (double)r * ceil_div(P, kTileKV) + causal_tile_visits(r);
+    }
+  }
+  const double t_sep = pairs * s.hq * 14.0 * s.d / kSepFlops;
+  const double t_fused = std::max(pairs * s.hq * 10.0 * s.d / kFusedFlops,
+                                  visits * s.hq * s.d * 4.0 / kAtomicBytes);
+  return t_fused < t_sep;
+}
+
 int validate_problem(const tree_attn_problem* p, bool need_device, Shape& s) {
   if (!p) return TREE_ATTN_ERR_INVALID;
+  if (p->dq_strategy < TREE_ATTN_DQ_AUTO || p->dq_strategy > TREE_ATTN_DQ_FUSED)
+    return TREE_ATTN_ERR_INVALID;
+  if (p->dq_strategy == TREE_ATTN_DQ_FUSED &&
+      (p->dtype != TREE_ATTN_BF16 || p->head_dim != 128))
+    return TREE_ATTN_ERR_UNSUPPORTED;
   if (p->dtype != TREE_ATTN_F32 && p->dtype != TREE_ATTN_BF16) return TREE_ATTN_ERR_UNSUPPORTED;
   if (p->head_dim != 64 && p->head_dim != 128) return TREE_ATTN_ERR_UNSUPPORTED;
   if (p->num_groups < 1 || p->num_branches < 0) return TREE_ATTN_ERR_INVALID;
@@ -197,6 +251,12 @@ int validate_problem(const tree_attn_problem* p, bool need_device, Shape& s) {
   if (s.k_items_replay * s.hkv > lim || s.part_rows > lim)
     return TREE_ATTN_ERR_INVALID;
   s.col_splits = choose_col_splits(s);
+  if (p->dq_strategy == TREE_ATTN_DQ_FUSED) {
+    s.fused_replay = s.fused_prefill = true;
+  } else if (p->dq_strategy == TREE_ATTN_DQ_AUTO && s.dtype == TREE_ATTN_BF16 && s.d == 128) {
+    s.fused_replay = choose_dq_fused(p, s, true);
+    s.fused_prefill = choose_dq_fused(p, s, false);
+  }
   // every attention launch must fit one dispatch: at most 2^32 - 1
   // work-items (workgroups x threads), counting the XCD round-up
   const long long n_hg = s.hq / s.hp;
@@ -268,6 +328,7 @@ struct Plan {
   float* o_part = nullptr;    // split prompt column: [chunks][r_tokens][hq][d]
   float* lse_part = nullptr;  // [chunks][hq][r_tokens]
   float* dq_part = nullptr;   // [chunks][r_tokens][hq][d]
+  float* dq_acc = nullptr;    // fused dQ strategy: float32 dQ / scale [tokens][hq][d]
   size_t bytes = 0;
 };
 
@@ -294,13 +355,18 @@ Plan make_plan(const Shape& s, int op, void* base) {
       }
       break;
     case TREE_ATTN_OP_REPLAY_BWD:
-      pl.mq = take_meta(c, s, s.q_items_replay * s.col_splits, sizeof(QItem));
-      if (s.col_splits > 1)
-        pl.dq_part = static_cast<float*>(
-            c.take((size_t)s.col_splits * s.r_tokens * s.hq * s.d * sizeof(float)));
-      pl.mk = take_meta(c, s, s.k_items_replay, sizeof(KItem));
-      pl.kt_p = c.take(kvT_p);
-      pl.kt_r = c.take(kvT_r);
+      if (s.fused_replay) {
+        pl.dq_acc = static_cast<float*>(c.take((size_t)s.r_tokens * s.hq * s.d * sizeof(float)));
+        pl.mk = take_meta(c, s, s.k_items_replay, sizeof(KItem));
+      } else {
+        pl.mq = take_meta(c, s, s.q_items_replay * s.col_splits, sizeof(QItem));
+        if (s.col_splits > 1)
+          pl.dq_part = static_cast<float*>(
+              c.take((size_t)s.col_splits * s.r_tokens * s.hq * s.d * sizeof(float)));
+        pl.mk = take_meta(c, s, s.k_items_replay, sizeof(KItem));
+        pl.kt_p = c.take(kvT_p);
+        pl.kt_r = c.take(kvT_r);
+      }
       pl.qt = c.take((size_t)s.hq * s.d * s.r_pad * e);
       pl.dot = c.take((size_t)s.hq * s.d * s.r_pad * e);
       pl.delta = static_cast<float*>(c.take((size_t)s.hq * s.r_tokens * sizeof(float)));
@@ -311,9 +377,13 @@ Plan make_plan(const Shape& s, int op, void* base) {
       }
       break;
     case TREE_ATTN_OP_PREFILL_BWD:
-      pl.mq = take_meta(c, s, s.q_items_prefill, sizeof(QItem));
+      if (s.fused_prefill) {
+        pl.dq_acc = static_cast<float*>(c.take((size_t)s.p_tokens * s.hq * s.d * sizeof(float)));
+      } else {
+        pl.mq = take_meta(c, s, s.q_items_prefill, sizeof(QItem));
+        pl.kt_p = c.take(kvT_p);
+      }
       pl.mk = take_meta(c, s, s.k_items_prefill, sizeof(KItem));
-      pl.kt_p = c.take(kvT_p);
       pl.qt = c.take((size_t)s.hq * s.d * s.p_pad * e);
       pl.dot = c.take((size_t)s.hq * s.d * s.p_pad * e);
       pl.delta = static_cast<float*>(c.take((size_t)s.hq * s.p_tokens * sizeof(float)));
@@ -634,8 +704,20 @@ int tree_attn_replay_bwd(const tree_attn_problem* problem, const void* k_p, cons
   (void)hipGetLastError();
   // K-stationary list first: it also writes both padded offset arrays.
   TA_TRY(run_meta(problem, s, pl.mk, kMetaKReplay, s.k_items_replay, st));
-  TA_TRY(run_meta(problem, s, pl.mq, kMetaQReplay, s.q_items_replay * s.col_splits, st));
-  if (s.r_tokens > 0) {
+  const bool fused = s.fused_replay && s.r_tokens > 0;
+  if (fused) {
+    // dQ from the dK/dV kernel: only the transposed Q and dO copies and the
+    // zeroed float32 accumulator are needed
+    TA_TRY(launch_row_dot(do_r, o_r, pl.delta, (int)s.r_tokens, s.hq, s.d, s.dtype, st));
+    TA_TRY(run_transpose(q_r, pl.qt, s.hq, s.hp, s, s.nb, problem->resp_cu_d, pl.mk.resp_pad,
+                         s.r_pad, st));
+    TA_TRY(run_transpose(do_r, pl.dot, s.hq, s.hp, s, s.nb, problem->resp_cu_d, pl.mk.resp_pad,
+                         s.r_pad, st));
+    TA_TRY(launch_zero(pl.dq_acc, s.r_tokens * s.hq * s.d, st));
+  } else if (!s.fused_replay) {  // (fused with no response row: nothing to do for dQ)
+    TA_TRY(run_meta(problem, s, pl.mq, kMetaQReplay, s.q_items_replay * s.col_splits, st));
+  }
+  if (s.r_tokens > 0 && !fused) {
     TA_TRY(launch_row_dot(do_r, o_r, pl.delta, (int)s.r_tokens, s.hq, s.d, s.dtype, st));
     TA_TRY(run_transpose(k_p, pl.kt_p, s.hkv, 1, s, s.ng, problem->prompt_cu_d,
                          pl.mq.prompt_pad, s.p_pad, st));
@@ -704,7 +786,11 @@ int tree_attn_replay_bwd(const tree_attn_problem* problem, const void* k_p, cons
     k.lse_stride = (int)s.r_tokens;
     k.qt_stride = (int)(s.r_pad * s.hp);
     k.scale = problem->softmax_scale;
+    k.dq_acc = fused ? pl.dq_acc : nullptr;
     TA_TRY(launch_dkv(k, st));
+    if (fused)
+      TA_TRY(launch_sum_parts(pl.dq_acc, 1, s.r_tokens * s.hq * s.d, dq_r, s.dtype, st,
+                              problem->softmax_scale));
     if (seeds && s.part_rows > 0) {
       SeedReduceArgs r;
       r.part_k = pl.part_k;
@@ -745,14 +831,17 @@ int tree_attn_prefill_bwd(const tree_attn_problem* problem, const void* q_p, con
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   TA_TRY(run_meta(problem, s, pl.mk, kMetaKPrefill, s.k_items_prefill, st));
-  TA_TRY(run_meta(problem, s, pl.mq, kMetaQPrefill, s.q_items_prefill, st));
+  const bool fused = s.fused_prefill;
+  if (!fused) TA_TRY(run_meta(problem, s, pl.mq, kMetaQPrefill, s.q_items_prefill, st));
   TA_TRY(launch_row_dot(do_p, o_p, pl.delta, (int)s.p_tokens, s.hq, s.d, s.dtype, st));
-  TA_TRY(run_transpose(k_p, pl.kt_p, s.hkv, 1, s, s.ng, problem->prompt_cu_d, pl.mq.prompt_pad,
-                       s.p_pad, st));
-  TA_TRY(run_transpose(q_p, pl.qt, s.hq, s.hp, s, s.ng, problem->prompt_cu_d, pl.mq.prompt_pad,
+  if (!fused)
+    TA_TRY(run_transpose(k_p, pl.kt_p, s.hkv, 1, s, s.ng, problem->prompt_cu_d, pl.mk.prompt_pad,
+                         s.p_pad, st));
+  TA_TRY(run_transpose(q_p, pl.qt, s.hq, s.hp, s, s.ng, problem->prompt_cu_d, pl.mk.prompt_pad,
                        s.p_pad, st));
   TA_TRY(run_transpose(do_p, pl.dot, s.hq, s.hp, s, s.ng, problem->prompt_cu_d,
-                       pl.mq.prompt_pad, s.p_pad, st));
+                       pl.mk.prompt_pad, s.p_pad, st));
+  if (fused) TA_TRY(launch_zero(pl.dq_acc, s.p_tokens * s.hq * s.d, st));
   DqLaunch q;
   q.q = q_p;
   q.dout = do_p;
@@ -777,7 +866,7 @@ int tree_attn_prefill_bwd(const tree_attn_problem* problem, const void* q_p, con
   q.kt_a_stride = (int)s.p_pad;
   q.kt_b_stride = (int)s.p_pad;
   q.scale = problem->softmax_scale;
-  TA_TRY(launch_dq(q, st));
+  if (!fused) TA_TRY(launch_dq(q, st));
   DkvLaunch k;
   k.k = k_p;
   k.v = v_p;
@@ -807,7 +896,11 @@ int tree_attn_prefill_bwd(const tree_attn_problem* problem, const void* q_p, con
   k.lse_stride = (int)s.p_tokens;
   k.qt_stride = (int)(s.p_pad * s.hp);
   k.scale = problem->softmax_scale;
+  k.dq_acc = fused ? pl.dq_acc : nullptr;
   TA_TRY(launch_dkv(k, st));
+  if (fused)
+    TA_TRY(launch_sum_parts(pl.dq_acc, 1, s.p_tokens * s.hq * s.d, dq_p, s.dtype, st,
+                            problem->softmax_scale));
   return TREE_ATTN_OK;
 }
 
@@ -823,6 +916,17 @@ int lse_merge(int32_t num_splits, int32_t rows, int32_t heads, int32_t head_dim,
   (void)hipGetLastError();
   TA_TRY(launch_lse_merge(num_splits, rows, heads, head_dim, out_dtype, o_parts, lse_parts, o_out,
                           lse_out, static_cast<hipStream_t>(stream)));
+  return TREE_ATTN_OK;
+}
+
+int tree_attn_dq_strategy_of(const tree_attn_problem* problem, int op, int* strategy) {
+  if (!strategy) return TREE_ATTN_ERR_INVALID;
+  if (op != TREE_ATTN_OP_REPLAY_BWD && op != TREE_ATTN_OP_PREFILL_BWD) return TREE_ATTN_ERR_INVALID;
+  Shape s;
+  const int rc = validate_problem(problem, false, s);
+  if (rc != TREE_ATTN_OK) return rc;
+  const bool fused = op == TREE_ATTN_OP_REPLAY_BWD ? s.fused_replay : s.fused_prefill;
+  *strategy = fused ? TREE_ATTN_DQ_FUSED : TREE_ATTN_DQ_SEPARATE;
   return TREE_ATTN_OK;
 }
 

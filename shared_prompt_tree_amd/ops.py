@@ -42,7 +42,12 @@ class Problem(ctypes.Structure):
         ("group_branch_cu_d", ctypes.c_void_p),
         ("resp_cu_h", ctypes.c_void_p),
         ("resp_cu_d", ctypes.c_void_p),
+        ("dq_strategy", ctypes.c_int32),
     ]
+
+
+# tree_attn_dq_strategy
+DQ_AUTO, DQ_SEPARATE, DQ_FUSED = 0, 1, 2
 
 
 _lib = None
@@ -71,10 +76,12 @@ def library():
     lib.tree_attn_error_string.restype = ctypes.c_char_p
     lib.tree_attn_last_hip_error.argtypes = []
     lib.tree_attn_set_kernel_events.argtypes = [ctypes.c_int, vp, vp]
+    lib.tree_attn_dq_strategy_of.argtypes = [P, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
     for name in ("tree_attn_workspace_size", "tree_attn_prefill", "tree_attn_replay_fwd",
                  "tree_attn_replay_fwd_noalloc",
                  "tree_attn_replay_bwd", "tree_attn_prefill_bwd", "lse_merge",
-                 "tree_attn_last_hip_error", "tree_attn_set_kernel_events"):
+                 "tree_attn_last_hip_error", "tree_attn_set_kernel_events",
+                 "tree_attn_dq_strategy_of"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -120,7 +127,7 @@ class TreeProblem:
     """
 
     def __init__(self, prompt_cu, group_branch_cu, resp_cu, num_q_heads, num_kv_heads,
-                 head_dim, dtype, softmax_scale=None, device=None):
+                 head_dim, dtype, softmax_scale=None, device=None, dq_strategy=DQ_AUTO):
         self.prompt_cu = np.ascontiguousarray(prompt_cu, dtype=np.int32)
         self.group_branch_cu = np.ascontiguousarray(group_branch_cu, dtype=np.int32)
         self.resp_cu = np.ascontiguousarray(resp_cu, dtype=np.int32)
@@ -147,13 +154,22 @@ class TreeProblem:
                                else self.group_branch_cu_d.data_ptr()),
             resp_cu_h=self.resp_cu.ctypes.data,
             resp_cu_d=None if self.resp_cu_d is None else self.resp_cu_d.data_ptr(),
+            dq_strategy=int(dq_strategy),
         )
 
+    @property
+    def dq_strategy(self):
+        return self.c.dq_strategy
+
+    @dq_strategy.setter
+    def dq_strategy(self, value):
+        self.c.dq_strategy = int(value)
+
     @classmethod
-    def from_tree(cls, tree, device=None, softmax_scale=None):
+    def from_tree(cls, tree, device=None, softmax_scale=None, dq_strategy=DQ_AUTO):
         from .workloads import torch_dtype
         return cls(tree.prompt_cu, tree.group_branch_cu, tree.resp_cu, tree.hq, tree.hkv, tree.d,
-                   torch_dtype(tree.dtype), softmax_scale, device)
+                   torch_dtype(tree.dtype), softmax_scale, device, dq_strategy)
 
     @property
     def prompt_tokens(self):
@@ -174,6 +190,15 @@ def tree_attn_set_kernel_events(kind, start=None, stop=None):
     s = None if start is None else ctypes.c_void_p(start.cuda_event)
     e = None if stop is None else ctypes.c_void_p(stop.cuda_event)
     _check("tree_attn_set_kernel_events", library().tree_attn_set_kernel_events(kind, s, e))
+
+
+def tree_attn_dq_strategy_of(problem: TreeProblem, op: int) -> int:
+    """DQ_SEPARATE or DQ_FUSED: the dQ strategy backward call ``op``
+    (OP_REPLAY_BWD or OP_PREFILL_BWD) uses for this problem."""
+    v = ctypes.c_int(-1)
+    _check("tree_attn_dq_strategy_of",
+           library().tree_attn_dq_strategy_of(ctypes.byref(problem.c), op, ctypes.byref(v)))
+    return v.value
 
 
 def tree_attn_workspace_size(problem: TreeProblem, op: int) -> int:

@@ -26,14 +26,27 @@ def device():
     return torch.device("cuda:0")
 
 
-def make_case(tree, seed, value_scale=1.0, zero_do_p=False):
+def make_case(tree, seed, value_scale=1.0, zero_do_p=False, dq_strategy=ops.DQ_SEPARATE):
     """Inputs on the GPU plus the problem descriptor."""
     dev = device()
     t = wl.make_tensors(tree, seed, device=dev, value_scale=value_scale)
     if zero_do_p:
         t["do_p"].zero_()
-    prob = ops.TreeProblem.from_tree(tree, device=dev)
+    prob = ops.TreeProblem.from_tree(tree, device=dev, dq_strategy=dq_strategy)
     return prob, t
+
+
+def fused_ok(tree):
+    """The fused dQ strategy covers bf16 with head_dim 128."""
+    return tree.dtype == "bf16" and tree.d == 128
+
+
+def strategies(tree):
+    """The dQ strategies a parity case runs: both where the fused one applies."""
+    return (ops.DQ_SEPARATE, ops.DQ_FUSED) if fused_ok(tree) else (ops.DQ_SEPARATE,)
+
+
+STRATEGY_NAME = {ops.DQ_SEPARATE: "separate dQ", ops.DQ_FUSED: "fused dQ"}
 
 
 def run_library(prob, t, seeds=True):

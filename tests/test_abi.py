@@ -273,3 +273,52 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(ops, "_lib", None)
     with pytest.raises(RuntimeError, match="not found"):
         ops.library()
+
+
+def test_dq_strategy_validation():
+    """dq_strategy outside the enum is invalid; the fused strategy covers
+    bf16 with head_dim 128 only."""
+    for bad in (-1, 3):
+        p = small_problem(dq_strategy=bad)
+        n = ctypes.c_size_t(0)
+        assert ops.library().tree_attn_workspace_size(ctypes.byref(p.c), 2, ctypes.byref(n)) == -1
+    for kw in (dict(head_dim=64), dict(dtype=torch.float32)):
+        p = small_problem(dq_strategy=ops.DQ_FUSED, **kw)
+        with pytest.raises(ops.TreeAttnError) as e:
+            ops.tree_attn_workspace_size(p, ops.OP_REPLAY_BWD)
+        assert e.value.code == -2
+    # automatic choice outside the fused strategy's domain: the separate pass
+    p = small_problem(head_dim=64)
+    assert ops.tree_attn_dq_strategy_of(p, ops.OP_REPLAY_BWD) == ops.DQ_SEPARATE
+
+
+def test_dq_strategy_workspaces():
+    """The fused strategy needs a float32 dQ accumulator instead of the
+    query-stationary work list and the K^T copies; each backward op reports
+    the strategy it uses, and the forward ops are not affected."""
+    sep = small_problem(prompt_cu=[0, 500, 900], resp_cu=[0, 300, 300, 700],
+                        dq_strategy=ops.DQ_SEPARATE)
+    fus = small_problem(prompt_cu=[0, 500, 900], resp_cu=[0, 300, 300, 700],
+                        dq_strategy=ops.DQ_FUSED)
+    for op in (ops.OP_PREFILL, ops.OP_REPLAY_FWD):
+        assert ops.tree_attn_workspace_size(sep, op) == ops.tree_attn_workspace_size(fus, op)
+    for op in (ops.OP_REPLAY_BWD, ops.OP_PREFILL_BWD):
+        assert ops.tree_attn_workspace_size(sep, op) != ops.tree_attn_workspace_size(fus, op)
+        assert ops.tree_attn_dq_strategy_of(sep, op) == ops.DQ_SEPARATE
+        assert ops.tree_attn_dq_strategy_of(fus, op) == ops.DQ_FUSED
+    with pytest.raises(ops.TreeAttnError):
+        ops.tree_attn_dq_strategy_of(sep, ops.OP_PREFILL)
+
+
+@pytest.mark.parametrize("name", ["prompt_heavy", "response_heavy", "long_mixed"])
+def test_dq_cost_model_prefers_separate_pass(name):
+    """Calibrated on same-box runs of both strategies: the fused kernel adds
+    2 bytes of float32 atomics per (row, key) pair at head_dim 128, which at
+    the measured ~0.95 TB/s takes longer than the separate pass's extra
+    matrix products, so the automatic choice is the separate pass on the
+    three large workloads."""
+    from shared_prompt_tree_amd import workloads as wl
+    tree = wl.make_tree(wl.SPECS[name])
+    p = ops.TreeProblem.from_tree(tree)
+    for op in (ops.OP_REPLAY_BWD, ops.OP_PREFILL_BWD):
+        assert ops.tree_attn_dq_strategy_of(p, op) == ops.DQ_SEPARATE

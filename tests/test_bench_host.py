@@ -154,3 +154,18 @@ def test_per_launch_traffic_report(tmp_profiles):
     assert launches[0]["hbm_read_bytes"] == 11e9
     none = bench.launch_report(tree, "dkv", [2.0, 20.0], None)
     assert none[0]["hbm_bytes"] is None and none[0]["algorithmic_bytes"] > 0
+
+
+def test_causal_tile_visits_closed_form():
+    """Key tiles read by the rows of a causal segment: the closed form equals
+    the brute-force sum of ceil(k / 256)."""
+    for n in (0, 1, 255, 256, 257, 511, 512, 1000, 32768, 32769):
+        assert bench.causal_tile_visits(n) == sum(-(-k // 256) for k in range(1, n + 1))
+
+
+def test_strategy_flops_per_pair():
+    """The fused dQ strategy moves the 6d of the dQ pass into the dK/dV
+    kernel as 2d: 10d in one kernel, none in the other; forward unchanged."""
+    assert bench.flops_per_pair_dim("dkv", True) == 10 and bench.flops_per_pair_dim("dq", True) == 0
+    assert bench.flops_per_pair_dim("dkv", False) == 8 and bench.flops_per_pair_dim("dq", False) == 6
+    assert bench.flops_per_pair_dim("fwd", True) == bench.flops_per_pair_dim("fwd", False) == 4

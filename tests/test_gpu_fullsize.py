@@ -18,6 +18,10 @@ sample, so that rows with a large norm cannot hide errors on others:
   partial seeds and their ordered sum); long-mixed: the last 64 prompt keys.
 Sum rules over all outputs: per group and kv head, sum_j dK_j = 0 and
 sum_j dV_j = sum of dO over the rows of the query heads that read it.
+
+Each workload runs with both dQ strategies (the separate dQ pass and the
+fused dK/dV/dQ kernel) on the same inputs; the automatic choice that the
+benchmark uses is one of the two, so its launch configuration is covered.
 """
 
 import math
@@ -28,8 +32,9 @@ import pytest
 import torch
 
 import oracle
+from shared_prompt_tree_amd import ops
 from shared_prompt_tree_amd import workloads as wl
-from tests._gpu import TOL, WORKERS, host64, make_case, rel_l2, run_library, say
+from tests._gpu import STRATEGY_NAME, TOL, WORKERS, host64, make_case, rel_l2, run_library, say
 
 pytestmark = pytest.mark.gpu
 
@@ -196,14 +201,21 @@ def test_full_size(name):
     scale = 1.0 / math.sqrt(tree.d)
     say(f"[full] {name}: {tree.prompt_tokens} prompt + {tree.resp_tokens} response tokens")
     prob, t = make_case(tree, spec.seed)
-    lib = run_library(prob, t)
-    for k, v in lib.items():
-        if v is not None:
-            assert bool(torch.isfinite(v).all()), k
-    say("[full] library done")
+    libs = {}
+    for st in (ops.DQ_SEPARATE, ops.DQ_FUSED):
+        prob.dq_strategy = st
+        libs[st] = run_library(prob, t)
+        for k, v in libs[st].items():
+            if v is not None:
+                assert bool(torch.isfinite(v).all()), (STRATEGY_NAME[st], k)
+    say("[full] library done (both dQ strategies)")
     rng = np.random.default_rng(spec.seed)
-    got = {k: [] for k in ("o", "lse", "dq", "dk", "dv")}
-    want = {k: [] for k in got}
+    want = {k: [] for k in ("o", "lse", "dq", "dk", "dv")}
+    got = {st: {k: [] for k in want} for st in libs}
+
+    def take(k, f):
+        for st, lib in libs.items():
+            got[st][k].append(host64(f(lib)))
 
     # sampled response rows and prompt rows
     for i in _sample_branches(tree, rng):
@@ -218,9 +230,9 @@ def test_full_size(name):
             rows = np.array([P + u for u in loc])
             o, lse, dq, _, _ = oracle.causal_unit(f["q"], f["k"], f["v"], f["do"], scale, rows=rows)
             tok = [int(tree.resp_cu[i]) + u for u in loc]
-            got["o"].append(host64(lib["o_r"][tok, h]))
-            got["lse"].append(host64(lib["lse_r"][h, tok]))
-            got["dq"].append(host64(lib["dq_r"][tok, h]))
+            take("o", lambda lib: lib["o_r"][tok, h])
+            take("lse", lambda lib: lib["lse_r"][h, tok])
+            take("dq", lambda lib: lib["dq_r"][tok, h])
             want["o"].append(o)
             want["lse"].append(lse)
             want["dq"].append(dq)
@@ -231,9 +243,9 @@ def test_full_size(name):
         loc = np.array(sorted({0, P - 1, P // 3, *rng.integers(0, P, size=5).tolist()}))
         o, lse, dq, _, _ = oracle.causal_unit(f["q"], f["k"], f["v"], f["do"], scale, rows=loc)
         tok = (int(tree.prompt_cu[g]) + loc).tolist()
-        got["o"].append(host64(lib["o_p"][tok, h]))
-        got["lse"].append(host64(lib["lse_p"][h, tok]))
-        got["dq"].append(host64(lib["dq_p"][tok, h]))
+        take("o", lambda lib: lib["o_p"][tok, h])
+        take("lse", lambda lib: lib["lse_p"][h, tok])
+        take("dq", lambda lib: lib["dq_p"][tok, h])
         want["o"].append(o)
         want["lse"].append(lse)
         want["dq"].append(dq)
@@ -258,8 +270,8 @@ def test_full_size(name):
             dk = dk + dk_h[P + r - n:]
             dv = dv + dv_h[P + r - n:]
         r1 = int(tree.resp_cu[i + 1])
-        got["dk"].append(host64(lib["dk_r"][r1 - n:r1, kv]))
-        got["dv"].append(host64(lib["dv_r"][r1 - n:r1, kv]))
+        take("dk", lambda lib: lib["dk_r"][r1 - n:r1, kv])
+        take("dv", lambda lib: lib["dv_r"][r1 - n:r1, kv])
         want["dk"].append(dk)
         want["dv"].append(dv)
 
@@ -270,14 +282,21 @@ def test_full_size(name):
     keys = np.array(sorted(set(range(min(n_first, P))) | set(range(max(0, P - n_last), P))))
     kv = int(rng.integers(0, tree.hkv))
     dk, dv = prompt_key_grads(tree, t, 0, kv, keys)
-    got["dk_p"] = [host64(lib["dk_p"][keys, kv])]
-    got["dv_p"] = [host64(lib["dv_p"][keys, kv])]
+    for st, lib in libs.items():
+        got[st]["dk_p"] = [host64(lib["dk_p"][keys, kv])]
+        got[st]["dv_p"] = [host64(lib["dv_p"][keys, kv])]
     want["dk_p"] = [dk]
     want["dv_p"] = [dv]
 
-    _check_sampled(name, got, want)
+    for st in libs:
+        _check_sampled(f"{name} [{STRATEGY_NAME[st]}]", got[st], want)
+    for st, lib in libs.items():
+        _sum_rules(f"{name} [{STRATEGY_NAME[st]}]", tree, t, lib)
 
-    # sum rules over every output, float64 on the GPU
+
+def _sum_rules(name, tree, t, lib):
+    """sum rules over every output, float64 on the GPU"""
+    rep = tree.hq // tree.hkv
     worst_k = worst_v = 0.0
     for g in range(tree.n_groups):
         p0, p1 = int(tree.prompt_cu[g]), int(tree.prompt_cu[g + 1])

@@ -11,33 +11,45 @@ import torch
 
 from shared_prompt_tree_amd import ops
 from shared_prompt_tree_amd import workloads as wl
-from tests._gpu import (TOL, compare, host64, make_case, oracle_inputs, rel_l2, run_library,
-                        run_oracle, say)
+from tests._gpu import (STRATEGY_NAME, TOL, compare, host64, make_case, oracle_inputs, rel_l2,
+                        run_library, run_oracle, say, strategies)
 
 pytestmark = pytest.mark.gpu
 
 
 def _case(tree, seed, value_scale=1.0, label="", zero_do_p=False):
+    """Runs the library with each applicable dQ strategy (separate pass, and
+    for bf16 / head_dim 128 also fused) and the oracle once.  Returns the
+    problem, the inputs, {strategy: outputs} and the oracle's outputs."""
     say(f"[case] {label} groups={tree.n_groups} hq={tree.hq} hkv={tree.hkv} d={tree.d} "
         f"dtype={tree.dtype} P={tree.prompt_lens} r={tree.resp_lens}")
     prob, t = make_case(tree, seed, value_scale, zero_do_p)
-    lib = run_library(prob, t)
+    libs = {}
+    for st in strategies(tree):
+        prob.dq_strategy = st
+        libs[st] = run_library(prob, t)
     ref = run_oracle(tree, t)
-    return prob, t, lib, ref
+    return prob, t, libs, ref
+
+
+def _compare_all(libs, ref, tol, label, tree, names=None):
+    for st, lib in libs.items():
+        kw = {} if names is None else {"names": names}
+        compare(lib, ref, tol, label=f"{label} [{STRATEGY_NAME[st]}]", tree=tree, **kw)
 
 
 def test_tiny_f32_full():
     spec = wl.SPECS["tiny"]
     tree = wl.make_tree(spec)
-    _, _, lib, ref = _case(tree, spec.seed, spec.value_scale, "tiny")
-    compare(lib, ref, TOL["f32"], label="tiny", tree=tree)
+    _, _, libs, ref = _case(tree, spec.seed, spec.value_scale, "tiny")
+    _compare_all(libs, ref, TOL["f32"], "tiny", tree)
 
 
 def test_small_bf16_full():
     spec = wl.SPECS["small"]
     tree = wl.make_tree(spec)
-    _, _, lib, ref = _case(tree, spec.seed, 1.0, "small")
-    compare(lib, ref, TOL["bf16"], label="small", tree=tree)
+    _, _, libs, ref = _case(tree, spec.seed, 1.0, "small")
+    _compare_all(libs, ref, TOL["bf16"], "small", tree)
 
 
 # Oracle-sized versions of the large shapes: the same heads, head_dim and
@@ -63,8 +75,8 @@ REDUCED["prompt column 12-wave"] = wl.Tree([1000], [[300] * 47 + [61]], 32, 8, 1
 @pytest.mark.parametrize("name", sorted(REDUCED))
 def test_reduced_shapes_full(name):
     tree = REDUCED[name]
-    _, _, lib, ref = _case(tree, 7, 1.0, name)
-    compare(lib, ref, TOL["bf16"], label=name, tree=tree)
+    _, _, libs, ref = _case(tree, 7, 1.0, name)
+    _compare_all(libs, ref, TOL["bf16"], name, tree)
 
 
 EDGE = {
@@ -118,8 +130,8 @@ EDGE = {
 def test_edge_cases(name):
     tree = EDGE[name]
     vs = 0.125 if tree.dtype == "f32" else 1.0
-    _, _, lib, ref = _case(tree, 11, vs, name)
-    compare(lib, ref, TOL[tree.dtype], label=name, tree=tree)
+    _, _, libs, ref = _case(tree, 11, vs, name)
+    _compare_all(libs, ref, TOL[tree.dtype], name, tree)
 
 
 @pytest.mark.parametrize("dtype,scale", [("bf16", 3.0), ("f32", 3.0)])
@@ -129,8 +141,8 @@ def test_peaked_scores(dtype, scale):
     forward's rescaling of O and the normaliser (taken only when a row's
     maximum grows by more than 2^8)."""
     tree = wl.Tree([700, 90], [[300, 129], [260]], 8, 2, 128 if dtype == "bf16" else 64, dtype)
-    _, _, lib, ref = _case(tree, 13, scale, f"peaked x{scale}")
-    compare(lib, ref, TOL[dtype], label=f"peaked {dtype}", tree=tree)
+    _, _, libs, ref = _case(tree, 13, scale, f"peaked x{scale}")
+    _compare_all(libs, ref, TOL[dtype], f"peaked {dtype}", tree)
 
 
 def _random_tree(seed):
@@ -157,8 +169,8 @@ def _random_tree(seed):
 def test_random_trees(seed):
     tree = _random_tree(1000 + seed)
     vs = 0.125 if tree.dtype == "f32" else 1.0
-    _, _, lib, ref = _case(tree, 50 + seed, vs, f"random {seed}")
-    compare(lib, ref, TOL[tree.dtype], label=f"random {seed}", tree=tree)
+    _, _, libs, ref = _case(tree, 50 + seed, vs, f"random {seed}")
+    _compare_all(libs, ref, TOL[tree.dtype], f"random {seed}", tree)
 
 
 def _random_split_tree(seed):
@@ -183,32 +195,39 @@ def _random_split_tree(seed):
 @pytest.mark.parametrize("seed", range(4))
 def test_random_split_trees(seed):
     tree = _random_split_tree(2000 + seed)
-    _, _, lib, ref = _case(tree, 70 + seed, 1.0, f"random split {seed}")
-    compare(lib, ref, TOL["bf16"], label=f"random split {seed}", tree=tree)
+    _, _, libs, ref = _case(tree, 70 + seed, 1.0, f"random split {seed}")
+    _compare_all(libs, ref, TOL["bf16"], f"random split {seed}", tree)
 
 
 def test_zero_prompt_upstream_gradient():
     """dO_P = 0: dQ_P must be exactly zero; everything else still matches."""
     tree = wl.Tree([500], [[200, 64]], 8, 2, 128, "bf16")
-    _, _, lib, ref = _case(tree, 5, 1.0, "dO_P=0", zero_do_p=True)
-    assert float(lib["dq_p"].abs().max()) == 0.0
+    _, _, libs, ref = _case(tree, 5, 1.0, "dO_P=0", zero_do_p=True)
+    for lib in libs.values():
+        assert float(lib["dq_p"].abs().max()) == 0.0
     names = [n for n in ("o_p", "lse_p", "o_r", "lse_r", "dk_p", "dv_p", "dq_r", "dk_r", "dv_r")]
-    compare(lib, ref, TOL["bf16"], names=names, label="dO_P=0", tree=tree)
+    _compare_all(libs, ref, TOL["bf16"], "dO_P=0", tree, names=names)
 
 
-def test_detached_prompt_seeds():
+@pytest.mark.parametrize("strategy", [ops.DQ_SEPARATE, ops.DQ_FUSED])
+def test_detached_prompt_seeds(strategy):
     """With no seeds, prefill backward returns only the prompt rows' own
-    term, i.e. the gradients of a tree whose groups have no branch."""
+    term, i.e. the gradients of a tree whose groups have no branch; the
+    response rows' dQ still includes their prompt column (the fused kernel
+    walks the prompt tiles for it without writing seeds)."""
     tree = wl.Tree([300, 129], [[100, 64], [50]], 4, 2, 128, "bf16")
-    prob, t = make_case(tree, 9)
+    prob, t = make_case(tree, 9, dq_strategy=strategy)
     lib = run_library(prob, t, seeds=False)
     prompt_only = wl.Tree(tree.prompt_lens, [[] for _ in tree.prompt_lens], 4, 2, 128, "bf16")
     ti = {k: v for k, v in t.items() if k.endswith("_p")}
     for k in ("q_r", "k_r", "v_r", "do_r"):
         ti[k] = t[k][:0]
     ref = run_oracle(prompt_only, ti)
-    compare(lib, ref, TOL["bf16"], names=("dq_p", "dk_p", "dv_p"), label="detached",
-            tree=tree)
+    label = f"detached [{STRATEGY_NAME[strategy]}]"
+    compare(lib, ref, TOL["bf16"], names=("dq_p", "dk_p", "dv_p"), label=label, tree=tree)
+    full = run_oracle(tree, t)
+    compare(lib, full, TOL["bf16"], names=("o_r", "lse_r", "dq_r", "dk_r", "dv_r"),
+            label=label, tree=tree)
 
 
 def test_detached_prompt_seeds_split():
@@ -226,16 +245,32 @@ def test_detached_prompt_seeds_split():
 
 
 def test_deterministic():
-    """No atomics on any output: two runs are bit-identical."""
+    """Separate dQ pass, no atomics on any output: two runs are
+    bit-identical."""
     for tree in (wl.Tree([700], [[300, 129, 64]], 8, 2, 128, "bf16"),
                  wl.Tree([64], [[128] * 6], 2, 1, 64, "bf16"),  # split prompt tiles
                  wl.Tree([8192], [[40, 33]], 8, 2, 128, "bf16")):  # split prompt column
-        prob, t = make_case(tree, 3)
+        prob, t = make_case(tree, 3, dq_strategy=ops.DQ_SEPARATE)
         a = run_library(prob, t)
         b = run_library(prob, t)
         for k, v in a.items():
             if v is not None:
                 assert torch.equal(v, b[k]), k
+
+
+def test_deterministic_fused_except_dq():
+    """Fused dQ: dQ is summed with atomics (rounding may differ between
+    runs); every other output stays bit-identical."""
+    for tree in (wl.Tree([700], [[300, 129, 64]], 8, 2, 128, "bf16"),
+                 wl.Tree([64], [[128] * 6], 2, 1, 128, "bf16")):  # split prompt tiles
+        prob, t = make_case(tree, 3, dq_strategy=ops.DQ_FUSED)
+        a = run_library(prob, t)
+        b = run_library(prob, t)
+        for k, v in a.items():
+            if v is not None and not k.startswith("dq"):
+                assert torch.equal(v, b[k]), k
+            elif v is not None:
+                assert rel_l2(host64(v), host64(b[k])) < 1e-3, k
 
 
 def test_lse_merge_matches_oracle():
