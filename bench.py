@@ -215,6 +215,11 @@ def parse():
                    help="instead of the benchmark: time the two backward calls with each dQ "
                         "strategy, alternating, on each workload of --workload and --also, "
                         "and print one JSON line")
+    p.add_argument("--split-sweep", action="store_true",
+                   help="instead of the benchmark: time the replay forward and backward "
+                        "calls of a few few-row replay shapes at forced prompt-column chunk "
+                        "counts (the data the column-split model's constants are fitted "
+                        "to), and print one JSON line")
     p.add_argument("--copy-calibration-mib", type=int, default=1024,
                    help="size of a plain device copy run after the timed region, used to "
                         "scale HBM byte counters in profiling runs (0 to skip)")
@@ -347,6 +352,10 @@ def measure_workload(name, steps, warmup, flattened=True, fms_hint=None, dq_stra
     stored = stored_launch_traffic(dom, name)
     fpd = sorted({flops_per_pair_dim(dom, fz) for fz in fused})
     rep["dq_strategy"] = {c: DQ_STRATEGY_NAMES[v] for c, v in used.items()}
+    # largest-first placement of the unsplit replay items of one head group /
+    # kv head onto one XCD's 32 CUs: makespan over mean load (1 = perfect)
+    rep["replay_schedule_balance"] = {k: round(wl.schedule_balance(tree, k), 4)
+                                      for k in ("dq", "dkv")}
     rep["roofline"] = {
         "kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
         "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
@@ -487,6 +496,72 @@ def dq_strategy_ab(names, steps):
                                              ("prefill_bwd", ops.OP_PREFILL_BWD))}
         out["workloads"].append(rec)
         del t, o_p, lse_p, o_r, lse_r, res
+        torch.cuda.empty_cache()
+    return out
+
+
+# Replay shapes where the prompt column split matters (32 query / 8 kv heads,
+# head_dim 128, bf16): (prompt, branch lengths).  The 520-workgroup shape is
+# two full rounds of 256 CUs plus 8 workgroups; 264 is one round plus 8.
+SPLIT_SWEEP_SHAPES = {
+    "13x260 behind 32768 (520 wg)": (32768, [260] * 13),
+    "8x512 behind 32768 (prompt-heavy replay, 512 wg)": (32768, [512] * 8),
+    "8x64 behind 131072 (64 wg)": (131072, [64] * 8),
+    "16x200 behind 65536 (512 wg)": (65536, [200] * 16),
+    "11x150 behind 2048 (264 wg)": (2048, [150] * 11),
+    # short prompt, many long branches: the prompt key tiles are split over
+    # branch ranges in the backward (not a column-split shape)
+    "24x4096 behind 256": (256, [4096] * 24),
+}
+SPLIT_SWEEP_S = (1, 2, 3, 4, 6, 8, 12, 16, 24, 32)
+
+
+def split_sweep(steps):
+    """Replay forward and backward (separate dQ pass) call times at forced
+    prompt-column chunk counts S, and the makespan model's own choice."""
+    import torch
+
+    from shared_prompt_tree_amd import ops
+    from shared_prompt_tree_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    out = {"metric": "replay call times by prompt-column chunks", "unit": "ms",
+           "steps": steps, "shapes": []}
+    for label, (P, rs) in SPLIT_SWEEP_SHAPES.items():
+        tree = wl.Tree([P], [rs], 32, 8, 128, "bf16")
+        t = wl.make_tensors(tree, 1, device=dev)
+        prob = ops.TreeProblem.from_tree(tree, device=dev, dq_strategy=ops.DQ_SEPARATE)
+        auto = {"replay_fwd": ops.tree_attn_prompt_col_splits_of(prob, ops.OP_REPLAY_FWD),
+                "replay_bwd": ops.tree_attn_prompt_col_splits_of(prob, ops.OP_REPLAY_BWD)}
+        rec = {"shape": label, "prompt": P, "branches": rs, "model_chooses": auto, "by_s": {}}
+        for S in SPLIT_SWEEP_S:
+            if S > max(1, -(-P // 64)):
+                continue
+            prob.prompt_col_splits = S
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+
+            def call():
+                o, lse = ops.tree_attn_replay_fwd(prob, t["k_p"], t["v_p"], t["q_r"], t["k_r"],
+                                                  t["v_r"])
+                e[1].record()
+                ops.tree_attn_replay_bwd(prob, t["k_p"], t["v_p"], t["q_r"], t["k_r"], t["v_r"],
+                                         o, lse, t["do_r"])
+
+            call()
+            torch.cuda.synchronize()
+            tf = tb = 0.0
+            for _ in range(steps):
+                e[0].record()
+                call()
+                e[2].record()
+                torch.cuda.synchronize()
+                tf += e[0].elapsed_time(e[1]) / steps
+                tb += e[1].elapsed_time(e[2]) / steps
+            rec["by_s"][S] = {"replay_fwd_ms": round(tf, 4), "replay_bwd_ms": round(tb, 4)}
+            print(f"[sweep] {label} S={S}: fwd {tf:.3f} ms, bwd {tb:.3f} ms", file=sys.stderr,
+                  flush=True)
+        out["shapes"].append(rec)
+        del t
         torch.cuda.empty_cache()
     return out
 
@@ -662,6 +737,9 @@ def main():
     from shared_prompt_tree_amd import ops
 
     ops.library()  # fail loudly if the HIP library is missing
+    if args.split_sweep:
+        print(json.dumps(split_sweep(args.steps)), flush=True)
+        return
     if args.dq_ab:
         names = [args.workload] + ([] if args.also in ("", "none") else
                                    [n for n in args.also.split(",") if n != args.workload])
@@ -703,6 +781,7 @@ def main():
             "kernel_tflops": a["kernel_tflops"], "roofline": a["roofline"],
             "phases": a["phases"], "useful_tflops_12d": a["useful_tflops_12d"],
             "dq_strategy": a["dq_strategy"],
+            "replay_schedule_balance": a["replay_schedule_balance"],
             "flattened_baseline": a.get("flattened_baseline"), "config": a["config"],
         })
         print(f"[bench] {aname}: {a['ms_per_step']:.2f} ms/step, {a['tflops']:.1f} TFLOP/s",
@@ -742,6 +821,7 @@ def main():
         "phases": main_rep["phases"],
         "useful_tflops_12d": main_rep["useful_tflops_12d"],
         "dq_strategy": main_rep["dq_strategy"],
+        "replay_schedule_balance": main_rep["replay_schedule_balance"],
         "roofline": main_rep["roofline"],
         "flattened_baseline": main_rep.get("flattened_baseline"),
         "cpu_baseline": cpu,

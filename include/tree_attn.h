@@ -130,6 +130,12 @@ typedef enum {
  * dq_strategy   a tree_attn_dq_strategy (0, the automatic choice, when the
  *               struct is zero-initialised); the workspace size depends on
  *               it, so size and call with the same value.
+ * prompt_col_splits  0: the library's makespan model picks, for each of the
+ *               replay query launches (forward, and dQ of the separate
+ *               strategy), how many chunks it cuts each prompt column into
+ *               (section 3.3: the chunks' partial states are merged); 1..64:
+ *               that many chunks for both (1 = not split), for measurements
+ *               and calibration.  The workspace size depends on it.
  */
 typedef struct {
   int32_t num_groups;
@@ -146,6 +152,7 @@ typedef struct {
   const int32_t* resp_cu_h;
   const int32_t* resp_cu_d;
   int32_t dq_strategy;
+  int32_t prompt_col_splits;
 } tree_attn_problem;
 
 /*
@@ -273,6 +280,16 @@ int lse_merge(int32_t num_splits, int32_t rows, int32_t heads, int32_t head_dim,
  * op; problem errors as tree_attn_workspace_size.
  */
 int tree_attn_dq_strategy_of(const tree_attn_problem* problem, int op, int* strategy);
+
+/*
+ * How many chunks the replay query launch of entry point `op` cuts each
+ * prompt column into for this problem (1 = not split): problem->
+ * prompt_col_splits when set, else the makespan model's choice for that
+ * launch.  op is TREE_ATTN_OP_REPLAY_FWD (the forward launch) or
+ * TREE_ATTN_OP_REPLAY_BWD (the dQ launch of the separate strategy; 1 under
+ * the fused strategy, which has none).  Writes *splits; no HIP call.
+ */
+int tree_attn_prompt_col_splits_of(const tree_attn_problem* problem, int op, int* splits);
 
 /* A static description of a tree_attn_status code. */
 const char* tree_attn_error_string(int code);

@@ -49,7 +49,8 @@ struct Shape {
   long long n_splits = 0;      // sum over groups of the splits
   long long part_rows = 0;     // partial-seed rows of the split groups
   int max_prompt = 0;          // longest prompt
-  int col_splits = 1;          // prompt-column chunks of the replay query lists
+  int col_splits_fwd = 1;      // prompt-column chunks of the replay forward launch
+  int col_splits_bwd = 1;      // and of the replay dQ launch
   long long own_work = 0;      // own-branch 64-key steps over the replay query tiles
   long long own_max = 0;       // most own-branch steps of one query tile
   long long prompt_work = 0;   // prompt-column 64-key steps over the replay query tiles
@@ -66,25 +67,39 @@ constexpr long long kSplitSlots = 512;
 // Replay query-stationary launches (forward, dQ) may cut each prompt column
 // into S chunks of whole 64-key tiles (each at least kMinChunkKeys keys);
 // the chunks' partial results are merged afterwards.  S is chosen by a
-// makespan model, in units of one 64-key step of one workgroup:
+// makespan model (the largest-first placement of section 3.4, Eq. 6, on 256
+// compute units, scored like Eqs. 7-10 with compute and movement terms), in
+// units of one 64-key step of one workgroup:
 //   items      q_wgs * S, each costing its prompt chunk, its own-branch
-//              tiles (last chunk only) and kItemOverhead;
+//              tiles (last chunk only) and an item overhead;
 //   makespan   max(rounds * mean item, longest item), rounds =
-//              ceil(items / kQSlots) (one 8-wave workgroup per CU);
+//              ceil(items / kQSlots) (one 8-wave workgroup per CU): the
+//              critical path of largest-first list scheduling, which the
+//              hardware dispatcher performs on the largest-first work list;
 //   merge      2 * S * response rows * Hq * d * 4 bytes of float32 partials
-//              written and read back, at kMergeBytesPerUnit per unit
-//              (HBM at ~5 TB/s against ~2 us per unit).
-// Only launches of up to kColSearchWgs workgroups are considered: beyond
-// that a partial last round costs little.
+//              written and read back, at a bytes-per-unit rate.
+// The forward and the dQ pass are priced separately (each entry point cuts
+// its own launch).  Their constants were fitted to bench.py --split-sweep:
+// replay calls of five few-row shapes timed at S = 1..32 on one MI355X
+// (forward: 1.7 us per unit, 6 units of overhead per workgroup, merge at
+// 0.275 ms/GB; dQ pass: 2.0 us per unit, no measurable overhead, merge at
+// 0.30 ms/GB; 2.7% and 3.2% rms error).  Only launches of up to
+// kColSearchWgs workgroups are considered: beyond that a partial last round
+// costs little.
 constexpr int kMinChunkKeys = 1024;
 constexpr int kMaxColSplits = 64;
 constexpr long long kQSlots = 256;
 constexpr long long kColSearchWgs = 8 * kQSlots;
-constexpr double kItemOverhead = 1.0;
-constexpr double kMergeBytesPerUnit = 1e7;
 
-// Prompt-column chunks S of the replay query lists (see the model above).
-int choose_col_splits(const Shape& s) {
+struct ColSplitCosts {
+  double item_overhead;         // units per workgroup
+  double merge_bytes_per_unit;  // partial bytes merged per unit of time
+};
+constexpr ColSplitCosts kFwdSplitCosts{6.0, 6.2e6};
+constexpr ColSplitCosts kDqSplitCosts{0.0, 6.7e6};
+
+// Prompt-column chunks S of a replay query launch (see the model above).
+int choose_col_splits(const Shape& s, const ColSplitCosts& c) {
   const long long n_hg = s.hq / s.hp;
   const long long q_wgs = s.q_items_replay * n_hg;
   const long long smax =
@@ -97,11 +112,11 @@ int choose_col_splits(const Shape& s) {
   double best_t = 0;
   for (long long S = 1; S <= smax; ++S) {
     const long long items = q_wgs * S;
-    const double work = prompt + own + kItemOverhead * items;
-    const double longest = (double)ceil_div(ptiles_max, S) + s.own_max + kItemOverhead;
+    const double work = prompt + own + c.item_overhead * items;
+    const double longest = (double)ceil_div(ptiles_max, S) + s.own_max + c.item_overhead;
     const double rounds = (double)ceil_div(items, kQSlots);
     double t = std::max(rounds * work / items, longest);
-    if (S > 1) t += 2.0 * S * row_bytes / kMergeBytesPerUnit;
+    if (S > 1) t += 2.0 * S * row_bytes / c.merge_bytes_per_unit;
     if (S == 1 || t < best_t) {
       best = (int)S;
       best_t = t;
@@ -250,7 +265,11 @@ int validate_problem(const tree_attn_problem* p, bool need_device, Shape& s) {
   if (s.p_pad * s.hp > lim || s.r_pad * s.hp > lim) return TREE_ATTN_ERR_INVALID;
   if (s.k_items_replay * s.hkv > lim || s.part_rows > lim)
     return TREE_ATTN_ERR_INVALID;
-  s.col_splits = choose_col_splits(s);
+  if (p->prompt_col_splits < 0 || p->prompt_col_splits > kMaxColSplits) return TREE_ATTN_ERR_INVALID;
+  s.col_splits_fwd = p->prompt_col_splits > 0 ? p->prompt_col_splits
+                                              : choose_col_splits(s, kFwdSplitCosts);
+  s.col_splits_bwd = p->prompt_col_splits > 0 ? p->prompt_col_splits
+                                              : choose_col_splits(s, kDqSplitCosts);
   if (p->dq_strategy == TREE_ATTN_DQ_FUSED) {
     s.fused_replay = s.fused_prefill = true;
   } else if (p->dq_strategy == TREE_ATTN_DQ_AUTO && s.dtype == TREE_ATTN_BF16 && s.d == 128) {
@@ -262,7 +281,9 @@ int validate_problem(const tree_attn_problem* p, bool need_device, Shape& s) {
   const long long n_hg = s.hq / s.hp;
   const long long dispatch_max = (long long)UINT32_MAX;
   const long long q_prefill = std::max(s.q_items_prefill * 512, s.wq_items_prefill * 768);
-  const long long q_replay = std::max(s.q_items_replay * s.col_splits * 512, s.wq_items_replay * 768);
+  const long long q_replay =
+      std::max(s.q_items_replay * std::max(s.col_splits_fwd, s.col_splits_bwd) * 512,
+               s.wq_items_replay * 768);
   if ((q_prefill + 8 * 768) * n_hg > dispatch_max || (q_replay + 8 * 768) * n_hg > dispatch_max)
     return TREE_ATTN_ERR_INVALID;
   if ((std::max(s.k_items_prefill, s.k_items_replay) + 8) * s.hkv * 512 > dispatch_max)
@@ -344,14 +365,14 @@ Plan make_plan(const Shape& s, int op, void* base) {
       pl.vt_p = c.take(kvT_p);
       break;
     case TREE_ATTN_OP_REPLAY_FWD:
-      pl.mq = take_meta(c, s, s.q_items_replay * s.col_splits, sizeof(QItem));
+      pl.mq = take_meta(c, s, s.q_items_replay * s.col_splits_fwd, sizeof(QItem));
       pl.vt_p = c.take(kvT_p);
       pl.vt_r = c.take(kvT_r);
-      if (s.col_splits > 1) {
+      if (s.col_splits_fwd > 1) {
         pl.o_part = static_cast<float*>(
-            c.take((size_t)s.col_splits * s.r_tokens * s.hq * s.d * sizeof(float)));
+            c.take((size_t)s.col_splits_fwd * s.r_tokens * s.hq * s.d * sizeof(float)));
         pl.lse_part = static_cast<float*>(
-            c.take((size_t)s.col_splits * s.hq * s.r_tokens * sizeof(float)));
+            c.take((size_t)s.col_splits_fwd * s.hq * s.r_tokens * sizeof(float)));
       }
       break;
     case TREE_ATTN_OP_REPLAY_BWD:
@@ -359,10 +380,10 @@ Plan make_plan(const Shape& s, int op, void* base) {
         pl.dq_acc = static_cast<float*>(c.take((size_t)s.r_tokens * s.hq * s.d * sizeof(float)));
         pl.mk = take_meta(c, s, s.k_items_replay, sizeof(KItem));
       } else {
-        pl.mq = take_meta(c, s, s.q_items_replay * s.col_splits, sizeof(QItem));
-        if (s.col_splits > 1)
+        pl.mq = take_meta(c, s, s.q_items_replay * s.col_splits_bwd, sizeof(QItem));
+        if (s.col_splits_bwd > 1)
           pl.dq_part = static_cast<float*>(
-              c.take((size_t)s.col_splits * s.r_tokens * s.hq * s.d * sizeof(float)));
+              c.take((size_t)s.col_splits_bwd * s.r_tokens * s.hq * s.d * sizeof(float)));
         pl.mk = take_meta(c, s, s.k_items_replay, sizeof(KItem));
         pl.kt_p = c.take(kvT_p);
         pl.kt_r = c.take(kvT_r);
@@ -427,7 +448,7 @@ int hip_status(hipError_t e) {
   } while (0)
 
 hipError_t run_meta(const tree_attn_problem* p, const Shape& s, const MetaBufs& m, int mode,
-                    long long cap, hipStream_t st, int tile_q = 0) {
+                    long long cap, hipStream_t st, int tile_q = 0, int col_splits = 1) {
   MetaArgs a;
   a.mode = mode;
   a.n_groups = s.ng;
@@ -443,7 +464,7 @@ hipError_t run_meta(const tree_attn_problem* p, const Shape& s, const MetaBufs& 
   a.items = m.items;
   a.cap = (int)cap;
   a.tile_q = tile_q > 0 ? tile_q : s.tile_q;
-  a.col_splits = mode == kMetaQReplay ? s.col_splits : 1;
+  a.col_splits = mode == kMetaQReplay ? col_splits : 1;
   a.split_target = mode == kMetaKReplay ? s.split_target : 0;
   a.split_cu = m.split_cu;
   a.split_first = m.split_first;
@@ -497,11 +518,11 @@ int run_replay_fwd(const tree_attn_problem* problem, const Shape& s, const Plan&
                    const void* v_r, void* o_r, float* lse_r, hipStream_t st) {
   if (s.r_tokens == 0) return TREE_ATTN_OK;
   (void)hipGetLastError();
-  const bool split = s.col_splits > 1;
-  const FwdShape fs = split ? FwdShape{8, s.tile_q, s.q_items_replay * s.col_splits}
+  const int S = s.col_splits_fwd;
+  const bool split = S > 1;
+  const FwdShape fs = split ? FwdShape{8, s.tile_q, s.q_items_replay * S}
                             : fwd_shape(s, s.q_items_replay, s.wq_items_replay);
-  TA_TRY(run_meta(problem, s, pl.mq, kMetaQReplay, s.q_items_replay * s.col_splits, st,
-                  fs.tile_q));
+  TA_TRY(run_meta(problem, s, pl.mq, kMetaQReplay, s.q_items_replay * S, st, fs.tile_q, S));
   TA_TRY(run_transpose(v_p, pl.vt_p, s.hkv, 1, s, s.ng, problem->prompt_cu_d, pl.mq.prompt_pad,
                        s.p_pad, st));
   TA_TRY(run_transpose(v_r, pl.vt_r, s.hkv, 1, s, s.nb, problem->resp_cu_d, pl.mq.resp_pad,
@@ -530,7 +551,7 @@ int run_replay_fwd(const tree_attn_problem* problem, const Shape& s, const Plan&
   f.lse_part = pl.lse_part;
   TA_TRY(launch_fwd(f, st));
   if (split)  // the chunks' partial states, merged (section 3.3)
-    TA_TRY(launch_lse_merge(s.col_splits, (int)s.r_tokens, s.hq, s.d, s.dtype, pl.o_part,
+    TA_TRY(launch_lse_merge(S, (int)s.r_tokens, s.hq, s.d, s.dtype, pl.o_part,
                             pl.lse_part, o_r, lse_r, st));
   return TREE_ATTN_OK;
 }
@@ -715,7 +736,8 @@ int tree_attn_replay_bwd(const tree_attn_problem* problem, const void* k_p, cons
                          s.r_pad, st));
     TA_TRY(launch_zero(pl.dq_acc, s.r_tokens * s.hq * s.d, st));
   } else if (!s.fused_replay) {  // (fused with no response row: nothing to do for dQ)
-    TA_TRY(run_meta(problem, s, pl.mq, kMetaQReplay, s.q_items_replay * s.col_splits, st));
+    TA_TRY(run_meta(problem, s, pl.mq, kMetaQReplay, s.q_items_replay * s.col_splits_bwd, st, 0,
+                    s.col_splits_bwd));
   }
   if (s.r_tokens > 0 && !fused) {
     TA_TRY(launch_row_dot(do_r, o_r, pl.delta, (int)s.r_tokens, s.hq, s.d, s.dtype, st));
@@ -740,7 +762,7 @@ int tree_attn_replay_bwd(const tree_attn_problem* problem, const void* k_p, cons
     q.v_b = v_r;
     q.kt_b = pl.kt_r;
     q.items = pl.mq.items;
-    q.n_items = (int)(s.q_items_replay * s.col_splits);
+    q.n_items = (int)(s.q_items_replay * s.col_splits_bwd);
     q.dq_part = pl.dq_part;
     q.hq = s.hq;
     q.hkv = s.hkv;
@@ -753,7 +775,7 @@ int tree_attn_replay_bwd(const tree_attn_problem* problem, const void* k_p, cons
     q.scale = problem->softmax_scale;
     TA_TRY(launch_dq(q, st));
     if (pl.dq_part)
-      TA_TRY(launch_sum_parts(pl.dq_part, s.col_splits, s.r_tokens * s.hq * s.d, dq_r, s.dtype,
+      TA_TRY(launch_sum_parts(pl.dq_part, s.col_splits_bwd, s.r_tokens * s.hq * s.d, dq_r, s.dtype,
                               st));
   }
   if (s.r_tokens > 0 || (seeds && s.p_tokens > 0)) {
@@ -916,6 +938,18 @@ int lse_merge(int32_t num_splits, int32_t rows, int32_t heads, int32_t head_dim,
   (void)hipGetLastError();
   TA_TRY(launch_lse_merge(num_splits, rows, heads, head_dim, out_dtype, o_parts, lse_parts, o_out,
                           lse_out, static_cast<hipStream_t>(stream)));
+  return TREE_ATTN_OK;
+}
+
+int tree_attn_prompt_col_splits_of(const tree_attn_problem* problem, int op, int* splits) {
+  if (!splits) return TREE_ATTN_ERR_INVALID;
+  if (op != TREE_ATTN_OP_REPLAY_FWD && op != TREE_ATTN_OP_REPLAY_BWD) return TREE_ATTN_ERR_INVALID;
+  Shape s;
+  const int rc = validate_problem(problem, false, s);
+  if (rc != TREE_ATTN_OK) return rc;
+  *splits = op == TREE_ATTN_OP_REPLAY_FWD ? s.col_splits_fwd
+            : s.fused_replay                ? 1  // no query-stationary dQ launch
+                                            : s.col_splits_bwd;
   return TREE_ATTN_OK;
 }
 

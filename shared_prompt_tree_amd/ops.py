@@ -43,6 +43,7 @@ class Problem(ctypes.Structure):
         ("resp_cu_h", ctypes.c_void_p),
         ("resp_cu_d", ctypes.c_void_p),
         ("dq_strategy", ctypes.c_int32),
+        ("prompt_col_splits", ctypes.c_int32),
     ]
 
 
@@ -77,11 +78,12 @@ def library():
     lib.tree_attn_last_hip_error.argtypes = []
     lib.tree_attn_set_kernel_events.argtypes = [ctypes.c_int, vp, vp]
     lib.tree_attn_dq_strategy_of.argtypes = [P, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+    lib.tree_attn_prompt_col_splits_of.argtypes = [P, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
     for name in ("tree_attn_workspace_size", "tree_attn_prefill", "tree_attn_replay_fwd",
                  "tree_attn_replay_fwd_noalloc",
                  "tree_attn_replay_bwd", "tree_attn_prefill_bwd", "lse_merge",
                  "tree_attn_last_hip_error", "tree_attn_set_kernel_events",
-                 "tree_attn_dq_strategy_of"):
+                 "tree_attn_dq_strategy_of", "tree_attn_prompt_col_splits_of"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -127,7 +129,8 @@ class TreeProblem:
     """
 
     def __init__(self, prompt_cu, group_branch_cu, resp_cu, num_q_heads, num_kv_heads,
-                 head_dim, dtype, softmax_scale=None, device=None, dq_strategy=DQ_AUTO):
+                 head_dim, dtype, softmax_scale=None, device=None, dq_strategy=DQ_AUTO,
+                 prompt_col_splits=0):
         self.prompt_cu = np.ascontiguousarray(prompt_cu, dtype=np.int32)
         self.group_branch_cu = np.ascontiguousarray(group_branch_cu, dtype=np.int32)
         self.resp_cu = np.ascontiguousarray(resp_cu, dtype=np.int32)
@@ -155,6 +158,7 @@ class TreeProblem:
             resp_cu_h=self.resp_cu.ctypes.data,
             resp_cu_d=None if self.resp_cu_d is None else self.resp_cu_d.data_ptr(),
             dq_strategy=int(dq_strategy),
+            prompt_col_splits=int(prompt_col_splits),
         )
 
     @property
@@ -164,6 +168,14 @@ class TreeProblem:
     @dq_strategy.setter
     def dq_strategy(self, value):
         self.c.dq_strategy = int(value)
+
+    @property
+    def prompt_col_splits(self):
+        return self.c.prompt_col_splits
+
+    @prompt_col_splits.setter
+    def prompt_col_splits(self, value):
+        self.c.prompt_col_splits = int(value)
 
     @classmethod
     def from_tree(cls, tree, device=None, softmax_scale=None, dq_strategy=DQ_AUTO):
@@ -198,6 +210,16 @@ def tree_attn_dq_strategy_of(problem: TreeProblem, op: int) -> int:
     v = ctypes.c_int(-1)
     _check("tree_attn_dq_strategy_of",
            library().tree_attn_dq_strategy_of(ctypes.byref(problem.c), op, ctypes.byref(v)))
+    return v.value
+
+
+def tree_attn_prompt_col_splits_of(problem: TreeProblem, op: int) -> int:
+    """Chunks per prompt column of the replay query launch of ``op``
+    (OP_REPLAY_FWD: the forward; OP_REPLAY_BWD: the dQ pass); 1 = not split."""
+    v = ctypes.c_int(-1)
+    _check("tree_attn_prompt_col_splits_of",
+           library().tree_attn_prompt_col_splits_of(ctypes.byref(problem.c), op,
+                                                    ctypes.byref(v)))
     return v.value
 
 

@@ -263,3 +263,65 @@ def flatten_tensors(tree: Tree, t):
                 parts[k].append(t[k + "_p"][p0:p1])
                 parts[k].append(t[k + "_r"][r0:r1])
     return {k + "_p": torch.cat(v) for k, v in parts.items()}
+
+
+# ------------------------------------------------------------ work balance
+#
+# Replay units and grid assignment (AugTree paper, section 3.4, Eq. 6): the
+# planner places units on lanes so as to minimise the largest lane load,
+# exactly for few units and by largest-first greedy balancing otherwise.  On
+# one GPU the lanes are compute units and the units are the workgroup items
+# of a launch; the device work lists are ordered largest first, and the
+# hardware dispatcher hands the next item to the next free compute unit,
+# which is that greedy rule applied online.  These helpers evaluate the
+# greedy placement on the host from item costs, to measure how far a launch
+# is from perfect balance.
+
+def assign_grid(costs, lanes):
+    """Largest-first greedy placement of units with the given costs onto
+    `lanes` lanes: each unit, in order of decreasing cost, goes to the lane
+    with the smallest load.  Returns the lane loads."""
+    import heapq
+
+    loads = [(0.0, j) for j in range(lanes)]
+    out = [0.0] * lanes
+    for c in sorted(costs, reverse=True):
+        load, j = heapq.heappop(loads)
+        out[j] = load + c
+        heapq.heappush(loads, (out[j], j))
+    return out
+
+
+def replay_items(tree: Tree, kind: str, hp: int):
+    """Costs of the replay work items of one head group (query-stationary
+    "dq": 64-key steps of each 256-row query tile, prompt column plus the
+    causal part of its branch) or one kv head (key-stationary "dkv": 32-row
+    query blocks each 256-key tile reads; a prompt tile reads every response
+    row of its group).  Unsplit launches."""
+    rows_tile = 256 // hp  # tokens per 256-row query tile
+    out = []
+    for p, rs in zip(tree.prompt_lens, tree.resp_lens):
+        if kind == "dkv":
+            rows = sum(rs)
+            out += [rows * hp / 32] * (-(-p // 256))
+            for r in rs:
+                out += [(r - 256 * t) * hp / 32 for t in range(-(-r // 256))]
+        else:
+            for r in rs:
+                for q0 in range(0, r, rows_tile):
+                    out.append(-(-p // 64) + -(-min(r, q0 + rows_tile) // 64))
+    return out
+
+
+def schedule_balance(tree: Tree, kind: str, lanes: int = 32):
+    """Largest-first makespan of the replay items of one head group or kv
+    head on the `lanes` compute units of one XCD, over their mean load (1 is
+    perfect balance; no placement can beat max(1, longest item / mean))."""
+    hp = 1
+    while hp < 16 and (tree.hq // tree.hkv) % (2 * hp) == 0:
+        hp *= 2
+    items = replay_items(tree, kind, hp)
+    if not items:
+        return 1.0
+    loads = assign_grid(items, lanes)
+    return max(loads) / (sum(items) / lanes)

@@ -177,30 +177,56 @@ def test_replay_workspace_holds_prompt_column_partials():
     assert split - whole >= partial
 
 
-def _column_chunks(prompt, branches, hq=32, hkv=8, d=128):
-    """Prompt-column chunks of a replay forward, read off its workspace: the
-    float32 partial O and LSE that only a split launch holds."""
-    def ws(p_len):
-        kw = dict(prompt_cu=[0, p_len], group_branch_cu=[0, len(branches)],
-                  resp_cu=np.concatenate([[0], np.cumsum(branches)]).tolist(),
-                  num_q_heads=hq, num_kv_heads=hkv, head_dim=d)
-        return ops.tree_attn_workspace_size(small_problem(**kw), ops.OP_REPLAY_FWD)
-    vt = lambda p_len: hkv * d * (-(-p_len // 64) * 64) * 2  # V^T copy of the prompt
-    r = int(np.sum(branches))
-    extra = ws(prompt) - ws(1000) - (vt(prompt) - vt(1000))  # 1000 keys cannot be cut
-    return extra / (r * hq * d * 4 + hq * r * 4)
+def _column_chunks(prompt, branches, op, hq=32, hkv=8, d=128):
+    """Prompt-column chunks of the replay forward (op 1) or dQ (op 2) launch."""
+    p = small_problem(prompt_cu=[0, prompt], group_branch_cu=[0, len(branches)],
+                      resp_cu=np.concatenate([[0], np.cumsum(branches)]).tolist(),
+                      num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                      dq_strategy=ops.DQ_SEPARATE)
+    return ops.tree_attn_prompt_col_splits_of(p, op)
+
+
+def _split_ws(prompt, branches, op, forced):
+    p = small_problem(prompt_cu=[0, prompt], group_branch_cu=[0, len(branches)],
+                      resp_cu=np.concatenate([[0], np.cumsum(branches)]).tolist(),
+                      num_q_heads=32, num_kv_heads=8, head_dim=128,
+                      dq_strategy=ops.DQ_SEPARATE, prompt_col_splits=forced)
+    return ops.tree_attn_workspace_size(p, op)
 
 
 def test_column_split_model():
-    """The prompt-column split follows the makespan model: 512 workgroups
-    (8 branches of 512 tokens, 32/8 heads) fill exactly two rounds of the
-    256 CUs and are not cut; 520 (13 branches of 260) would need a third,
-    nearly empty round, so the column is cut (into 6 chunks); a few rows
-    behind a 131072-token prompt are cut until the items fit one round."""
-    assert _column_chunks(32768, [512] * 8) == pytest.approx(0, abs=0.05)
-    assert _column_chunks(32768, [260] * 13) == pytest.approx(6, abs=0.05)
-    assert _column_chunks(131072, [64] * 8) == pytest.approx(4, abs=0.05)
-    assert _column_chunks(2048, [150] * 11) == pytest.approx(2, abs=0.05)
+    """The prompt-column split follows the makespan model, priced separately
+    for the forward and the dQ launch with constants fitted to measured
+    sweeps (bench.py --split-sweep).  On those sweeps the choices below were
+    the fastest measured S or within 2.5% of it: 512 workgroups (8 branches
+    of 512, 32/8 heads) fill two rounds of the 256 CUs and are not cut; 520
+    (13 of 260) are cut into 4 (forward) and 6 (dQ) chunks; a few rows
+    behind a 131072-token prompt into 4; 264 workgroups behind a 2048-token
+    prompt only in the dQ pass."""
+    assert _column_chunks(32768, [512] * 8, 1) == 1 and _column_chunks(32768, [512] * 8, 2) == 1
+    assert _column_chunks(32768, [260] * 13, 1) == 4 and _column_chunks(32768, [260] * 13, 2) == 6
+    assert _column_chunks(131072, [64] * 8, 1) == 4 and _column_chunks(131072, [64] * 8, 2) == 4
+    assert _column_chunks(2048, [150] * 11, 1) == 1 and _column_chunks(2048, [150] * 11, 2) == 2
+
+
+def test_forced_column_splits():
+    """prompt_col_splits forces the chunk count of both launches (the
+    workspace grows by the float32 partials); beyond 64 it is invalid; the
+    query reports 1 for the dQ launch of the fused strategy, which has none."""
+    base = _split_ws(32768, [512] * 8, ops.OP_REPLAY_FWD, 1)
+    assert _split_ws(32768, [512] * 8, ops.OP_REPLAY_FWD, 3) > base
+    assert (_split_ws(32768, [512] * 8, ops.OP_REPLAY_BWD, 3)
+            > _split_ws(32768, [512] * 8, ops.OP_REPLAY_BWD, 1))
+    p = small_problem(prompt_col_splits=5)
+    assert ops.tree_attn_prompt_col_splits_of(p, ops.OP_REPLAY_FWD) == 5
+    assert ops.tree_attn_prompt_col_splits_of(p, ops.OP_REPLAY_BWD) == 5
+    p.dq_strategy = ops.DQ_FUSED
+    assert ops.tree_attn_prompt_col_splits_of(p, ops.OP_REPLAY_BWD) == 1
+    for bad in (-1, 65):
+        with pytest.raises(ops.TreeAttnError):
+            ops.tree_attn_workspace_size(small_problem(prompt_col_splits=bad), ops.OP_REPLAY_FWD)
+    with pytest.raises(ops.TreeAttnError):
+        ops.tree_attn_prompt_col_splits_of(small_problem(), ops.OP_PREFILL)
 
 
 def test_bad_op_and_null_out_pointer():

@@ -114,9 +114,10 @@ EDGE = {
     # finds worth their merge; forward partials merged by lse_merge, dQ
     # partials summed.  4 workgroups -> 8 chunks of 1024 keys here.
     "split prompt column": wl.Tree([8192], [[40, 33]], 8, 2, 128, "bf16"),
-    # 264 workgroups: one more than a full round of 256 CUs, so the model
+    # 264 workgroups: one more than a full round of 256 CUs; the dQ launch
     # cuts the 2048-key prompt into 2 chunks (3 rounds of half-length items
-    # instead of 2 rounds of whole ones).
+    # instead of 2 rounds of whole ones), the forward, with its larger
+    # per-workgroup overhead, does not: the two launches differ.
     "split prompt column past a full round": wl.Tree([2048], [[150] * 11], 32, 8, 128, "bf16"),
     # 6 workgroups -> 4 chunks; prompts of 47 and 79 tiles, an empty branch.
     "split prompt column, two groups": wl.Tree([3000, 5000], [[17, 0, 64], [100]], 4, 2, 64,
@@ -197,6 +198,19 @@ def test_random_split_trees(seed):
     tree = _random_split_tree(2000 + seed)
     _, _, libs, ref = _case(tree, 70 + seed, 1.0, f"random split {seed}")
     _compare_all(libs, ref, TOL["bf16"], f"random split {seed}", tree)
+
+
+@pytest.mark.parametrize("splits", [2, 5, 64])
+def test_forced_prompt_col_splits(splits):
+    """Forced prompt-column chunk counts, up to more chunks than the 47
+    prompt tiles (the extra chunks hold no prompt key: empty partial states,
+    the identity of the merge)."""
+    tree = wl.Tree([3000], [[100, 37]], 8, 2, 128, "bf16")
+    prob, t = make_case(tree, 17)
+    prob.prompt_col_splits = splits
+    lib = run_library(prob, t)
+    ref = run_oracle(tree, t)
+    compare(lib, ref, TOL["bf16"], label=f"forced S={splits}", tree=tree)
 
 
 def test_zero_prompt_upstream_gradient():
