@@ -220,6 +220,10 @@ def parse():
                         "calls of a few few-row replay shapes at forced prompt-column chunk "
                         "counts (the data the column-split model's constants are fitted "
                         "to), and print one JSON line")
+    p.add_argument("--tile-split-sweep", action="store_true",
+                   help="instead of the benchmark: time the replay backward of short-prompt, "
+                        "many-branch shapes at forced prompt-tile split targets (the data the "
+                        "split rule is fitted to), and print one JSON line")
     p.add_argument("--copy-calibration-mib", type=int, default=1024,
                    help="size of a plain device copy run after the timed region, used to "
                         "scale HBM byte counters in profiling runs (0 to skip)")
@@ -566,6 +570,85 @@ def split_sweep(steps):
     return out
 
 
+# Short-prompt, many-branch replays: a prompt key tile reads every response
+# row of its group, so it is split over branch ranges.  (prompt, [branch
+# lengths per group]) with 32 query / 8 kv heads, head_dim 128, bf16; the
+# response-heavy workload itself is measured too.
+TILE_SPLIT_SHAPES = {
+    "24x4096 behind 256": (256, [[4096] * 24]),
+    "2 groups of 32x1024 behind 512": (512, [[1024] * 32, [1024] * 32]),
+    "16x2048 behind 1024": (1024, [[2048] * 16]),
+    "8 groups of 8x512 behind 128": (128, [[512] * 8] * 8),
+}
+# split rule targets tried: max(longest branch, rows read by all key tiles x
+# Hkv / slots) for these slot counts, and no split
+TILE_SPLIT_SLOTS = (64, 128, 256, 512, 1024, 2048, 4096)
+
+
+def key_rows_total(tree):
+    """Rows read by all key-stationary replay items of one kv head: each own
+    tile the rows of its branch at or after it, each prompt tile every row
+    of its group."""
+    total = 0
+    for p, rs in zip(tree.prompt_lens, tree.resp_lens):
+        for r in rs:
+            n = -(-r // 256)
+            total += n * r - 256 * n * (n - 1) // 2
+        total += -(-p // 256) * sum(rs)
+    return total
+
+
+def tile_split_sweep(steps):
+    """Replay backward call times at forced prompt-tile split targets, and
+    the rule's own choice."""
+    import torch
+
+    from shared_prompt_tree_amd import ops
+    from shared_prompt_tree_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    out = {"metric": "replay backward call time by prompt-tile split target", "unit": "ms",
+           "steps": steps, "shapes": []}
+    shapes = dict(TILE_SPLIT_SHAPES)
+    shapes["response_heavy"] = None
+    for label, shp in shapes.items():
+        if shp is None:
+            tree = wl.make_tree(wl.SPECS["response_heavy"])
+        else:
+            tree = wl.Tree([shp[0]] * len(shp[1]), shp[1], 32, 8, 128, "bf16")
+        t = wl.make_tensors(tree, 2, device=dev)
+        prob = ops.TreeProblem.from_tree(tree, device=dev, dq_strategy=ops.DQ_SEPARATE)
+        o, lse = ops.tree_attn_replay_fwd(prob, t["k_p"], t["v_p"], t["q_r"], t["k_r"], t["v_r"])
+        longest = max((r for rs in tree.resp_lens for r in rs), default=1)
+        total = key_rows_total(tree)
+        targets = {f"slots {n}": max(longest, -(-total * tree.hkv // n)) for n in TILE_SPLIT_SLOTS}
+        targets["no split"] = max(sum(rs) for rs in tree.resp_lens)
+        rec = {"shape": label, "rule_splits": ops.tree_attn_prompt_tile_splits_of(prob),
+               "by_target": {}}
+        for name, tgt in targets.items():
+            prob.prompt_tile_split_rows = int(tgt)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ops.tree_attn_replay_bwd(prob, t["k_p"], t["v_p"], t["q_r"], t["k_r"], t["v_r"], o,
+                                     lse, t["do_r"])
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(steps):
+                ops.tree_attn_replay_bwd(prob, t["k_p"], t["v_p"], t["q_r"], t["k_r"], t["v_r"],
+                                         o, lse, t["do_r"])
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / steps
+            rec["by_target"][name] = {"rows": int(tgt),
+                                      "splits": ops.tree_attn_prompt_tile_splits_of(prob),
+                                      "replay_bwd_ms": round(ms, 4)}
+            print(f"[tile-sweep] {label} {name} (target {tgt}, splits "
+                  f"{rec['by_target'][name]['splits']}): {ms:.3f} ms", file=sys.stderr, flush=True)
+        out["shapes"].append(rec)
+        del t, o, lse
+        torch.cuda.empty_cache()
+    return out
+
+
 def causal_tile_visits(n, tile=256):
     """Key tiles read by the rows of an n-token causal segment:
     sum over k = 1..n of ceil(k / tile)."""
@@ -737,6 +820,9 @@ def main():
     from shared_prompt_tree_amd import ops
 
     ops.library()  # fail loudly if the HIP library is missing
+    if args.tile_split_sweep:
+        print(json.dumps(tile_split_sweep(args.steps)), flush=True)
+        return
     if args.split_sweep:
         print(json.dumps(split_sweep(args.steps)), flush=True)
         return

@@ -136,6 +136,14 @@ typedef enum {
  *               (section 3.3: the chunks' partial states are merged); 1..64:
  *               that many chunks for both (1 = not split), for measurements
  *               and calibration.  The workspace size depends on it.
+ * prompt_tile_split_rows  0: the library's rule picks how the replay
+ *               backward splits a group's prompt key tiles over ranges of its
+ *               branches (each range a work item writing float32 partial
+ *               seeds, added in a fixed order); r > 0: each range reads at
+ *               most r response rows (whole branches, at least one each;
+ *               a value at or above a group's rows leaves it unsplit), for
+ *               measurements and calibration.  The workspace size depends
+ *               on it.
  */
 typedef struct {
   int32_t num_groups;
@@ -153,6 +161,7 @@ typedef struct {
   const int32_t* resp_cu_d;
   int32_t dq_strategy;
   int32_t prompt_col_splits;
+  int32_t prompt_tile_split_rows;
 } tree_attn_problem;
 
 /*
@@ -290,6 +299,14 @@ int tree_attn_dq_strategy_of(const tree_attn_problem* problem, int op, int* stra
  * the fused strategy, which has none).  Writes *splits; no HIP call.
  */
 int tree_attn_prompt_col_splits_of(const tree_attn_problem* problem, int op, int* splits);
+
+/*
+ * Work items the replay backward cuts the groups' prompt key tiles into,
+ * per prompt tile position, summed over groups: n_g when no group is split,
+ * more when some are (problem->prompt_tile_split_rows when set, else the
+ * library's rule).  Writes *splits; no HIP call.
+ */
+int tree_attn_prompt_tile_splits_of(const tree_attn_problem* problem, int* splits);
 
 /* A static description of a tree_attn_status code. */
 const char* tree_attn_error_string(int code);

@@ -61,7 +61,11 @@ struct Shape {
 // A replay key-stationary item reading more than the launch's total rows
 // divided by this is worth splitting: with one dK/dV workgroup per compute
 // unit of a 256-CU MI355X, no item then exceeds half of one CU's fair share,
-// so the largest-first order can balance the launch.
+// so the largest-first order can balance the launch.  Measured
+// (bench.py --tile-split-sweep, five short-prompt shapes and the
+// response-heavy workload): every value from 256 to 4096 is within 2-6% of
+// the best split target, and 512 within 2% on all of them; not splitting
+// costs up to 1.9x.
 constexpr long long kSplitSlots = 512;
 
 // Replay query-stationary launches (forward, dQ) may cut each prompt column
@@ -251,7 +255,10 @@ int validate_problem(const tree_attn_problem* p, bool need_device, Shape& s) {
       s.prompt_work += ceil_div(p->resp_cu_h[i + 1] - p->resp_cu_h[i], s.tile_q) *
                        ceil_div(plen, kTileK);
   }
-  s.split_target = std::max(longest, (total * s.hkv + kSplitSlots - 1) / kSplitSlots);
+  if (p->prompt_tile_split_rows < 0) return TREE_ATTN_ERR_INVALID;
+  s.split_target = p->prompt_tile_split_rows > 0
+                       ? (long long)p->prompt_tile_split_rows
+                       : std::max(longest, (total * s.hkv + kSplitSlots - 1) / kSplitSlots);
   for (int g = 0; g < ng; ++g) {
     const int plen = p->prompt_cu_h[g + 1] - p->prompt_cu_h[g];
     const int branches = p->group_branch_cu_h[g + 1] - p->group_branch_cu_h[g];
@@ -950,6 +957,15 @@ int tree_attn_prompt_col_splits_of(const tree_attn_problem* problem, int op, int
   *splits = op == TREE_ATTN_OP_REPLAY_FWD ? s.col_splits_fwd
             : s.fused_replay                ? 1  // no query-stationary dQ launch
                                             : s.col_splits_bwd;
+  return TREE_ATTN_OK;
+}
+
+int tree_attn_prompt_tile_splits_of(const tree_attn_problem* problem, int* splits) {
+  if (!splits) return TREE_ATTN_ERR_INVALID;
+  Shape s;
+  const int rc = validate_problem(problem, false, s);
+  if (rc != TREE_ATTN_OK) return rc;
+  *splits = (int)s.n_splits;
   return TREE_ATTN_OK;
 }
 

@@ -44,6 +44,7 @@ class Problem(ctypes.Structure):
         ("resp_cu_d", ctypes.c_void_p),
         ("dq_strategy", ctypes.c_int32),
         ("prompt_col_splits", ctypes.c_int32),
+        ("prompt_tile_split_rows", ctypes.c_int32),
     ]
 
 
@@ -79,11 +80,13 @@ def library():
     lib.tree_attn_set_kernel_events.argtypes = [ctypes.c_int, vp, vp]
     lib.tree_attn_dq_strategy_of.argtypes = [P, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
     lib.tree_attn_prompt_col_splits_of.argtypes = [P, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+    lib.tree_attn_prompt_tile_splits_of.argtypes = [P, ctypes.POINTER(ctypes.c_int)]
     for name in ("tree_attn_workspace_size", "tree_attn_prefill", "tree_attn_replay_fwd",
                  "tree_attn_replay_fwd_noalloc",
                  "tree_attn_replay_bwd", "tree_attn_prefill_bwd", "lse_merge",
                  "tree_attn_last_hip_error", "tree_attn_set_kernel_events",
-                 "tree_attn_dq_strategy_of", "tree_attn_prompt_col_splits_of"):
+                 "tree_attn_dq_strategy_of", "tree_attn_prompt_col_splits_of",
+                 "tree_attn_prompt_tile_splits_of"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -130,7 +133,7 @@ class TreeProblem:
 
     def __init__(self, prompt_cu, group_branch_cu, resp_cu, num_q_heads, num_kv_heads,
                  head_dim, dtype, softmax_scale=None, device=None, dq_strategy=DQ_AUTO,
-                 prompt_col_splits=0):
+                 prompt_col_splits=0, prompt_tile_split_rows=0):
         self.prompt_cu = np.ascontiguousarray(prompt_cu, dtype=np.int32)
         self.group_branch_cu = np.ascontiguousarray(group_branch_cu, dtype=np.int32)
         self.resp_cu = np.ascontiguousarray(resp_cu, dtype=np.int32)
@@ -159,6 +162,7 @@ class TreeProblem:
             resp_cu_d=None if self.resp_cu_d is None else self.resp_cu_d.data_ptr(),
             dq_strategy=int(dq_strategy),
             prompt_col_splits=int(prompt_col_splits),
+            prompt_tile_split_rows=int(prompt_tile_split_rows),
         )
 
     @property
@@ -176,6 +180,14 @@ class TreeProblem:
     @prompt_col_splits.setter
     def prompt_col_splits(self, value):
         self.c.prompt_col_splits = int(value)
+
+    @property
+    def prompt_tile_split_rows(self):
+        return self.c.prompt_tile_split_rows
+
+    @prompt_tile_split_rows.setter
+    def prompt_tile_split_rows(self, value):
+        self.c.prompt_tile_split_rows = int(value)
 
     @classmethod
     def from_tree(cls, tree, device=None, softmax_scale=None, dq_strategy=DQ_AUTO):
@@ -220,6 +232,15 @@ def tree_attn_prompt_col_splits_of(problem: TreeProblem, op: int) -> int:
     _check("tree_attn_prompt_col_splits_of",
            library().tree_attn_prompt_col_splits_of(ctypes.byref(problem.c), op,
                                                     ctypes.byref(v)))
+    return v.value
+
+
+def tree_attn_prompt_tile_splits_of(problem: TreeProblem) -> int:
+    """Prompt key-tile work items per tile position, summed over groups
+    (n_g when no group's prompt tiles are split over branch ranges)."""
+    v = ctypes.c_int(-1)
+    _check("tree_attn_prompt_tile_splits_of",
+           library().tree_attn_prompt_tile_splits_of(ctypes.byref(problem.c), ctypes.byref(v)))
     return v.value
 
 

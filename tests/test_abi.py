@@ -348,3 +348,15 @@ def test_dq_cost_model_prefers_separate_pass(name):
     p = ops.TreeProblem.from_tree(tree)
     for op in (ops.OP_REPLAY_BWD, ops.OP_PREFILL_BWD):
         assert ops.tree_attn_dq_strategy_of(p, op) == ops.DQ_SEPARATE
+
+
+def test_forced_prompt_tile_split_rows():
+    """prompt_tile_split_rows sets the split target: one branch per range at
+    1 row, the group unsplit at or above its rows; negative is invalid."""
+    kw = dict(prompt_cu=[0, 64], group_branch_cu=[0, 6], resp_cu=[0, 128, 256, 384, 512, 640, 768],
+              num_q_heads=2, num_kv_heads=1, head_dim=64)
+    assert ops.tree_attn_prompt_tile_splits_of(small_problem(prompt_tile_split_rows=1, **kw)) == 6
+    assert ops.tree_attn_prompt_tile_splits_of(small_problem(prompt_tile_split_rows=768, **kw)) == 1
+    assert ops.tree_attn_prompt_tile_splits_of(small_problem(prompt_tile_split_rows=300, **kw)) == 3
+    with pytest.raises(ops.TreeAttnError):
+        ops.tree_attn_workspace_size(small_problem(prompt_tile_split_rows=-1), ops.OP_REPLAY_BWD)

@@ -213,6 +213,19 @@ def test_forced_prompt_col_splits(splits):
     compare(lib, ref, TOL["bf16"], label=f"forced S={splits}", tree=tree)
 
 
+@pytest.mark.parametrize("rows", [1, 150, 10 ** 6])
+def test_forced_prompt_tile_split_rows(rows):
+    """Forced prompt-tile split targets: one branch per range (1), ranges of
+    a few branches (150), no split (10^6); uneven branches with an empty one,
+    two groups."""
+    tree = wl.Tree([300, 40], [[100, 5, 300, 0, 64, 200], [50, 60]], 4, 2, 128, "bf16")
+    prob, t = make_case(tree, 19)
+    prob.prompt_tile_split_rows = rows
+    lib = run_library(prob, t)
+    ref = run_oracle(tree, t)
+    compare(lib, ref, TOL["bf16"], label=f"forced split rows {rows}", tree=tree)
+
+
 def test_zero_prompt_upstream_gradient():
     """dO_P = 0: dQ_P must be exactly zero; everything else still matches."""
     tree = wl.Tree([500], [[200, 64]], 8, 2, 128, "bf16")
