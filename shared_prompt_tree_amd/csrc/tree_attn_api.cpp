@@ -64,7 +64,7 @@ struct Shape {
 // so the largest-first order can balance the launch.  Measured
 // (bench.py --tile-split-sweep, five short-prompt shapes and the
 // response-heavy workload): every value from 256 to 4096 is within 2-6% of
-// the best split target, and 512 within 2% on all of them; not splitting
+// the best split target, and 512 within 2.1% on all of them; not splitting
 // costs up to 1.9x.
 constexpr long long kSplitSlots = 512;
 
