@@ -7,9 +7,11 @@
 // (token, head) pair: the hp query heads of a token that share one kv head
 // are packed next to each other, so every K/V tile staged in LDS feeds all of
 // them (GQA reuse).  Each wave owns 32 rows and keeps their Q in registers.
-// Keys stream through LDS in tiles of 64, double buffered: first segment A
-// (no mask: a replay row sees the whole prompt), then segment B (causal with
-// diagonal: prefill over the prompt, or the row's own branch in replay).  One
+// Keys stream through LDS in tiles of 64 (bf16: triple buffered, the tile
+// loop software-pipelined in 32-key halves; float32: double buffered): first
+// segment A (no mask: a replay row sees the whole prompt), then segment B
+// (causal with diagonal: prefill over the prompt, or the row's own branch in
+// replay).  One
 // online-softmax state per row runs across both segments, so the prompt
 // column and the own-branch part are merged in registers (section 3.3: the
 // partial states along a query row are merged associatively).
@@ -26,6 +28,8 @@
 namespace treeattn {
 
 constexpr float kRescale = 8.0f;  // log2 units
+// bf16 launches use the software-pipelined tile loop.
+constexpr bool kFwdPipe = true;
 
 template <typename T, int D>
 struct FwdArgs {
@@ -46,9 +50,12 @@ struct FwdArgs {
   float* lse_part;  // [chunks][hq][tokens]
 };
 
-template <typename T, int D, int NW>
+// PIPE (bf16): the tile loop runs software-pipelined in 32-key halves, with
+// three LDS stages (see the PIPE branch below).
+template <typename T, int D, int NW, bool PIPE = false>
 __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs<T, D> a) {
   constexpr int NT = 64 * NW, KT = kTileK, CH = ChunkOf<T>::kElems;
+  constexpr int NSTAGE = PIPE ? 3 : 2;
   constexpr int NCHK = D / CH;        // 16-byte chunks per K row
   constexpr int NCHV = KT / CH;       // chunks per V^T row
   constexpr int KROW = tile_row_elems<T, NCHK>();  // padded row lengths
@@ -89,8 +96,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs<T, D> a) {
   const int total = na + nb;
   const size_t kv_stride = (size_t)a.hkv * D;
 
-  // Tile j into LDS stage j % 2: K rows (keys past the segment are clamped to
-  // its last key and masked later) and V^T rows (padded copy, always in range).
+  // Tile j into LDS stage j % NSTAGE: K rows (keys past the segment are
+  // clamped to its last key and masked later) and V^T rows (padded copy,
+  // always in range).
   auto gload = [&](int j) {
     const bool inA = j < na;
     const int ks = (inA ? j : j - na) * KT;
@@ -100,7 +108,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs<T, D> a) {
     const int vstride = inA ? a.vt_a_stride : a.vt_b_stride;
     const T* vbase = inA ? a.vt_a + (size_t)kv * D * a.vt_a_stride + it.apad + ks
                          : a.vt_b + (size_t)kv * D * a.vt_b_stride + it.bpad + ks;
-    T* kt = smem + (j & 1) * STAGE;
+    T* kt = smem + (j % NSTAGE) * STAGE;
     g2l_tile<T, KT, NCHK, NT>(kt, kbase, [&](int r) { return min(r, klast) * (int)kv_stride; });
     g2l_tile<T, D, NCHV, NT>(kt + KTILE, vbase, [&](int r) { return r * vstride; });
   };
@@ -116,6 +124,122 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs<T, D> a) {
   const float c2 = a.scale_log2;
   const int wave_tok0 = (32 * w) / a.hp;  // smallest token index of this wave
 
+  if constexpr (PIPE) {
+    // Half h = 2 j + e covers keys 32 e .. 32 e + 31 of tile j.  Per half:
+    //   phase A  the scores of half h + 1 (8 products, K fragments loaded
+    //            one step ahead) with the softmax of half h issued between
+    //            them: mask, row maximum, lazy rescale, P = exp2(S - m),
+    //            bf16 conversion and the normaliser sum;
+    //   phase B  O^T += V^T P^T for half h (8 products).
+    // Tile j + 1's K is read in the second half of tile j, so tiles are
+    // triple buffered.  After the first half of tile j every wave waits for
+    // its copies of tile j + 1 and meets the others at one barrier; by then
+    // tile j - 1 is no longer read, and tile j + 2 is copied into its stage.
+    const int nhalf = 2 * total;
+    if (total > 0) gload(0);
+    if (total > 1) gload(1);
+    wait_vmem();
+    __syncthreads();
+    f32x16 s_cur = f32x16{}, s_nxt = f32x16{};
+    Frag<T> kf[2];
+    auto kload = [&](int hh, int kk, int slot) {
+      const T* kt = smem + ((hh >> 1) % NSTAGE) * STAGE;
+      lds_frag(kf[slot], kt, 32 * (hh & 1) + lr, KROW, 16 * kk + 8 * lh);
+    };
+    if (nhalf > 0) {
+      kload(0, 0, 0);
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        if (kk + 1 < NKK) kload(0, kk + 1, (kk + 1) & 1);
+        mma(s_cur, kf[kk & 1], qf[kk]);
+      }
+    }
+    for (int h = 0; h < nhalf; ++h) {
+      const int j = h >> 1, e = h & 1;
+      const bool more = h + 1 < nhalf;
+      const bool inA = j < na;
+      const int kb0 = (inA ? j : j - na) * KT + 32 * e;  // first key of the half
+      const bool need_mask = inA ? (kb0 + 32 > it.alen) : (kb0 + 31 > it.qpos + wave_tok0);
+      const int lim = inA ? it.alen - 1 : it.qpos + tok;
+      s_nxt = f32x16{};
+      // The next half's scores are formed unconditionally so that phase A
+      // stays straight-line code; after the item's last half they come from
+      // a stage that is in bounds but stale, and are discarded.
+      const int hn = more ? h + 1 : h;
+      kload(hn, 0, 0);
+      Frag<T> pf[2];
+      float mx = -INFINITY, m_use = 0.f;
+      // phase A: scores of half h + 1 beside the softmax of half h
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        if (kk + 1 < NKK) kload(hn, kk + 1, (kk + 1) & 1);
+        mma(s_nxt, kf[kk & 1], qf[kk]);
+        if (kk == 0) {
+          if (need_mask) {
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj) {
+              const int key = kb0 + 8 * (jj >> 2) + 4 * lh + (jj & 3);
+              if (key > lim) s_cur[jj] = -INFINITY;
+            }
+          }
+#pragma unroll
+          for (int jj = 0; jj < 16; ++jj) mx = fmaxf(mx, s_cur[jj]);
+          mx = max_with_other_half(mx) * c2;
+        } else if (kk == 1) {
+          // lazy rescale (as in the tile loop below)
+          if (__any(mx > m_run + kRescale)) {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
+            lsum *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+            m_run = m_new;
+          }
+        } else {
+          m_use = (m_run == -INFINITY) ? 0.f : m_run;
+          constexpr int PER = 16 / (NKK - 2);  // exponentials per remaining step
+          const int base = (kk - 2) * PER;
+#pragma unroll
+          for (int u = 0; u < PER; ++u)
+            if (base + u < 16) s_cur[base + u] = fast_exp2(s_cur[base + u] * c2 - m_use);
+          if (kk == NKK - 1) {
+#pragma unroll
+            for (int jj = (NKK - 2) * PER; jj < 16; ++jj)
+              s_cur[jj] = fast_exp2(s_cur[jj] * c2 - m_use);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      float ps = 0.f;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        to_frag(pf[hf], s_cur, 8 * hf);
+        ps = frag_sum(pf[hf], ps);
+      }
+      lsum += ps;
+      // phase B: O^T += V^T P^T for half h
+      {
+        const T* vt = smem + (j % NSTAGE) * STAGE + KTILE;
+        Frag<T> vf[2];
+        auto vload = [&](int st, int slot) {  // st = 2*db + hf
+          lds_frag(vf[slot], vt, 32 * (st >> 1) + lr, VROW, 16 * (2 * e + (st & 1)) + 8 * lh);
+        };
+        vload(0, 0);
+#pragma unroll
+        for (int st = 0; st < 2 * NDB; ++st) {
+          if (st + 1 < 2 * NDB) vload(st + 1, (st + 1) & 1);
+          mma(oacc[st >> 1], vf[st & 1], pf[st & 1]);
+        }
+      }
+      s_cur = s_nxt;
+      if (e == 0) {
+        // tile j + 1 complete everywhere, tile j - 1 no longer read
+        wait_vmem();
+        __syncthreads();
+        if (j + 2 < total) gload(j + 2);
+      }
+    }
+  } else {
   if (total > 0) gload(0);
   wait_vmem();
   __syncthreads();
@@ -245,6 +369,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs<T, D> a) {
     wait_vmem();
     __syncthreads();
   }
+  }
 
   const float lt = sum_with_other_half(lsum);
   if (!qvalid) return;
@@ -288,7 +413,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs<T, D> a) {
   if (lh == 0) a.lse[(size_t)head * a.lse_stride + it.q0 + tok] = lse;
 }
 
-template <typename T, int D, int NW>
+template <typename T, int D, int NW, bool PIPE = false>
 static hipError_t launch_fwd_t(const FwdLaunch& l, hipStream_t s) {
   FwdArgs<T, D> a;
   a.q = static_cast<const T*>(l.q);
@@ -311,25 +436,29 @@ static hipError_t launch_fwd_t(const FwdLaunch& l, hipStream_t s) {
   a.o_part = l.o_part;
   a.lse_part = l.lse_part;
   constexpr int CH = 16 / sizeof(T);
-  const size_t smem =
-      2 * sizeof(T) * (size_t)(tile_elems<T, kTileK, D / CH>() + tile_elems<T, D, kTileK / CH>());
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fwd_kernel<T, D, NW>),
+  const size_t smem = (PIPE ? 3 : 2) * sizeof(T) *
+                      (size_t)(tile_elems<T, kTileK, D / CH>() + tile_elems<T, D, kTileK / CH>());
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fwd_kernel<T, D, NW, PIPE>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
   const int grid = xcd_grid(l.n_items, a.n_hg);
   if (grid <= 0) return hipSuccess;
   hipEvent_t e0, e1;
   kernel_events(kKernelFwd, &e0, &e1);
-  if (e0) hipExtLaunchKernelGGL(fwd_kernel<T, D, NW>, dim3(grid), dim3(64 * NW), smem, s, e0, e1, 0, a);
-  else fwd_kernel<T, D, NW><<<dim3(grid), dim3(64 * NW), smem, s>>>(a);
+  if (e0)
+    hipExtLaunchKernelGGL(fwd_kernel<T, D, NW, PIPE>, dim3(grid), dim3(64 * NW), smem, s, e0, e1,
+                          0, a);
+  else fwd_kernel<T, D, NW, PIPE><<<dim3(grid), dim3(64 * NW), smem, s>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd(const FwdLaunch& l, hipStream_t s) {
   if (l.dtype == 1) {
     if (l.waves == 12)
-      return l.d == 128 ? launch_fwd_t<bf16, 128, 12>(l, s) : launch_fwd_t<bf16, 64, 12>(l, s);
-    return l.d == 128 ? launch_fwd_t<bf16, 128, 8>(l, s) : launch_fwd_t<bf16, 64, 8>(l, s);
+      return l.d == 128 ? launch_fwd_t<bf16, 128, 12, kFwdPipe>(l, s)
+                        : launch_fwd_t<bf16, 64, 12, kFwdPipe>(l, s);
+    return l.d == 128 ? launch_fwd_t<bf16, 128, 8, kFwdPipe>(l, s)
+                      : launch_fwd_t<bf16, 64, 8, kFwdPipe>(l, s);
   }
   return l.d == 128 ? launch_fwd_t<float, 128, 8>(l, s) : launch_fwd_t<float, 64, 8>(l, s);
 }
