@@ -788,6 +788,26 @@ def summarize(dirs, command):
                 v = sum(float(r["Counter_Value"]) for r in other[c] if sym in r["Kernel_Name"])
                 row.append(f"{c}={v:.4g}")
             lines.append(f"{kind}: " + " ".join(row))
+        if "GRBM_GUI_ACTIVE" in other:
+            # Engine clock while each kernel ran: GRBM_GUI_ACTIVE sums the
+            # active cycles of the 8 XCDs at the engine clock, over the
+            # dispatch's own start/end timestamps (ns).  The plain copy is a
+            # reference that does not load the matrix units.
+            rows = other["GRBM_GUI_ACTIVE"]
+            if rows and "Start_Timestamp" in rows[0]:
+                lines.append("")
+                lines.append("engine clock while the kernel ran (GRBM_GUI_ACTIVE / 8 / dispatch "
+                             "time), GHz:")
+                for kind, sym in list(KERNEL_SYMBOLS.items()) + [("copy", "copyBuffer")]:
+                    rs = [r for r in rows if sym in r["Kernel_Name"]]
+                    if kind == "copy" and rs:  # the 1 GiB calibration copy only
+                        rs = [max(rs, key=lambda r: int(r["End_Timestamp"]) -
+                                  int(r["Start_Timestamp"]))]
+                    ns = sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rs)
+                    if ns > 0:
+                        cyc = sum(float(r["Counter_Value"]) for r in rs) / 8
+                        lines.append(f"{kind}: {cyc / ns:.3f} over {len(rs)} dispatches, "
+                                     f"{ns / 1e6:.3f} ms")
         if "SQ_VALU_MFMA_BUSY_CYCLES" in other and "GRBM_GUI_ACTIVE" in other:
             # GRBM_GUI_ACTIVE sums the active cycles of the 8 XCDs; each of the
             # 1024 SIMDs can keep its matrix unit busy for all of them.

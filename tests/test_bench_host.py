@@ -79,6 +79,21 @@ def test_mfma_busy_share(tmp_profiles):
     assert not os.listdir(bench.PROFILES)
 
 
+def test_engine_clock(tmp_profiles):
+    # 8 XCDs of 2.0e9 cycles each over one second is 2.0 GHz; two dispatches
+    # of one kernel are pooled by cycles and time.
+    def row(kernel, cycles, t0, t1):
+        r = _ctr(kernel, "GRBM_GUI_ACTIVE", cycles)
+        r.update(Start_Timestamp=str(t0), End_Timestamp=str(t1))
+        return r
+    _write_csv(tmp_profiles / "c" / "run_counter_collection.csv", [
+        row(DKV, 8 * 2.0e6, 0, 1_000_000), row(DKV, 8 * 1.0e6, 5_000_000, 5_500_000),
+        row(COPY, 8 * 2.4e5, 0, 100_000), row(COPY, 8 * 500, 0, 100)])
+    text = bench.summarize([str(tmp_profiles / "c")], "c")
+    assert "dkv: 2.000 over 2 dispatches, 1.500 ms" in text
+    assert "copy: 2.400 over 1 dispatches" in text
+
+
 def test_kernel_stats_table(tmp_profiles):
     _write_csv(tmp_profiles / "k" / "run_kernel_stats.csv", [
         {"Name": DKV, "Calls": "4", "AverageNs": "2500000", "TotalDurationNs": "10000000",

@@ -146,6 +146,70 @@ def test_peaked_scores(dtype, scale):
     _compare_all(libs, ref, TOL[dtype], f"peaked {dtype}", tree)
 
 
+def _key_ramp(tree, t, rising, span=0.75, qa=4.0):
+    """Queries carry qa * u and keys f_j * u for one direction u per kv head,
+    where key j of a row's key sequence (the prompt, then its own branch) has
+    f_j rising from 0 to `span` over the longest sequence, or falling from
+    it.  Rising, a row's scores grow by about qa * span * |u|^2 / sqrt(d)
+    (~49 log2 units at head_dim 128) from its first keys to its last, so the
+    forward's running maximum keeps growing past its lazy-rescale threshold;
+    falling, later probabilities underflow instead.  The softmax still
+    spreads over dozens of keys."""
+    gen = torch.Generator().manual_seed(29)
+    dev = t["q_p"].device
+    grp = tree.hq // tree.hkv
+    u = torch.randn(tree.hkv, tree.d, generator=gen).to(dev)
+    longest = max(p + max(rs, default=0) for p, rs in zip(tree.prompt_lens, tree.resp_lens))
+
+    def weight(pos):
+        f = torch.tensor(pos, dtype=torch.float32, device=dev) / max(longest - 1, 1) * span
+        return f if rising else span - f
+
+    pos_p, pos_r = [], []
+    for p, rs in zip(tree.prompt_lens, tree.resp_lens):
+        pos_p += list(range(p))
+        for r in rs:
+            pos_r += [p + j for j in range(r)]
+    for name, pos in (("k_p", pos_p), ("k_r", pos_r)):
+        k = t[name]
+        if k.shape[0]:
+            k.copy_((weight(pos)[:, None, None] * u[None] + 0.5 * k.float()).to(k.dtype))
+    uq = u.repeat_interleave(grp, dim=0)
+    for name in ("q_p", "q_r"):
+        q = t[name]
+        if q.shape[0]:
+            q.copy_((qa * uq[None] + 0.5 * q.float()).to(q.dtype))
+
+
+@pytest.mark.parametrize("dtype,rising", [("bf16", True), ("bf16", False), ("f32", True)])
+def test_key_ramp_scores(dtype, rising):
+    """Scores that rise (or fall) steadily along every row's keys: the rising
+    case drives the forward's rescale of O and the normaliser many times per
+    row (its running maximum grows by more than 2^8 again and again), on
+    prompt rows and on response rows behind the prompt column.
+
+    Gated: the forward outputs and dV.  dQ and dK are not: with keys sharing
+    one large direction, dS summing to zero along each row cancels that
+    direction in dQ (and the queries' in dK), so bf16 rounding of dS - the
+    operand every bf16 backward multiplies with - stands in front of a small
+    remainder.  Their error here (up to ~3e-2 on a segment) is that input's
+    conditioning, not a rescale path: the backward kernels have none, they
+    use the final LSE.  Backward parity under peaked scores is covered by
+    test_peaked_scores."""
+    tree = wl.Tree([700, 90], [[300, 129], [260]], 8, 2, 128 if dtype == "bf16" else 64, dtype)
+    label = f"key ramp {'rising' if rising else 'falling'} {dtype}"
+    say(f"[case] {label}")
+    prob, t = make_case(tree, 17, 0.25 if dtype == "f32" else 1.0)
+    _key_ramp(tree, t, rising)
+    libs = {}
+    for st in strategies(tree):
+        prob.dq_strategy = st
+        libs[st] = run_library(prob, t)
+    ref = run_oracle(tree, t)
+    _compare_all(libs, ref, TOL[dtype], label, tree,
+                 names=("o_p", "lse_p", "o_r", "lse_r", "dv_p", "dv_r"))
+
+
 def _random_tree(seed):
     """A small random batch of trees: 1-3 groups, 0-6 branches each,
     prompts of 0-300 tokens and branches of 0-260 (zero-length ones
