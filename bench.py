@@ -22,8 +22,18 @@ Prints one JSON line.  Besides the headline numbers it carries:
                      parallelism does it: every (prompt, response) pair as
                      its own causal sequence, with the same kernels
   cpu_baseline       the float64 oracle on a bounded sample, host cores
+  mfma_ceiling       measured after the timed work: the GPU's sustained dense
+                     bf16 MFMA rate on register operands, constant and random
+                     (data like the attention operands), and each kernel's
+                     rate over the random-operand figure
   also               the same measurement for further workloads (response-heavy
                      and long-mixed by default; long-mixed with 3 timed steps)
+
+Other modes print one JSON line of their own instead: --dq-ab (the two dQ
+strategies), --split-sweep and --tile-split-sweep (the data the replay
+load-balancing models are fitted to), --mfma-ceiling (the sustained bf16
+MFMA rate of the GPU on register operands); --summarize writes profiles/
+summaries from rocprofv3 output.
 """
 
 from __future__ import annotations
@@ -224,6 +234,13 @@ def parse():
                    help="instead of the benchmark: time the replay backward of short-prompt, "
                         "many-branch shapes at forced prompt-tile split targets (the data the "
                         "split rule is fitted to), and print one JSON line")
+    p.add_argument("--mfma-ceiling", action="store_true",
+                   help="instead of the benchmark: the sustained dense bf16 MFMA rate of "
+                        "this GPU on register operands (libmfmaceiling.so), with constant and "
+                        "with random bf16 operands, and print one JSON line")
+    p.add_argument("--ceiling-seconds", type=float, default=2.0,
+                   help="how long the MFMA-rate measurement runs each operand kind (after "
+                        "the timed work in a benchmark run, 0 to skip; or in --mfma-ceiling)")
     p.add_argument("--copy-calibration-mib", type=int, default=1024,
                    help="size of a plain device copy run after the timed region, used to "
                         "scale HBM byte counters in profiling runs (0 to skip)")
@@ -598,6 +615,40 @@ def key_rows_total(tree):
     return total
 
 
+def mfma_ceiling(seconds):
+    """Sustained dense bf16 MFMA rate on register operands: the instruction
+    rate (constant operands) and what the power limit allows on data like
+    the attention operands (random bf16 values of variance ~1).  The second
+    is the ceiling the kernels' matrix work runs against."""
+    import ctypes
+
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "shared_prompt_tree_amd",
+                        "lib", "libmfmaceiling.so")
+    if not os.path.exists(path):
+        fail(f"{path} is missing: build it with python -m shared_prompt_tree_amd.build")
+    lib = ctypes.CDLL(path)
+    lib.mfma_ceiling_run.argtypes = [ctypes.c_int, ctypes.c_double,
+                                     ctypes.POINTER(ctypes.c_double),
+                                     ctypes.POINTER(ctypes.c_double),
+                                     ctypes.POINTER(ctypes.c_int)]
+    lib.mfma_ceiling_run.restype = ctypes.c_int
+    out = {"metric": "sustained dense bf16 MFMA rate, register operands, 2 waves/SIMD",
+           "unit": "TFLOP/s", "peak": round(PEAK_BF16_TFLOPS, 1), "seconds_each": seconds}
+    for kind, rnd in (("constant", 0), ("random", 1)):
+        tf, first, n = ctypes.c_double(), ctypes.c_double(), ctypes.c_int()
+        rc = lib.mfma_ceiling_run(rnd, seconds, ctypes.byref(tf), ctypes.byref(first),
+                                  ctypes.byref(n))
+        if rc != 0:
+            fail(f"mfma_ceiling_run({kind}) failed with {rc}")
+        out[kind] = {"tflops": round(tf.value, 1),
+                     "pct_of_peak": round(100 * tf.value / PEAK_BF16_TFLOPS, 1),
+                     "first_launch_tflops": round(first.value, 1), "launches": n.value}
+        print(f"[ceiling] {kind} operands: {tf.value:.1f} TFLOP/s "
+              f"({100 * tf.value / PEAK_BF16_TFLOPS:.1f}% of peak; first launch "
+              f"{first.value:.1f}) over {n.value} launches", file=sys.stderr, flush=True)
+    return out
+
+
 def tile_split_sweep(steps):
     """Replay backward call times at forced prompt-tile split targets, and
     the rule's own choice."""
@@ -780,9 +831,12 @@ def summarize(dirs, command):
             json.dump(rec, fh, indent=1)
     other = {c: v for c, v in counters.items() if c not in ("FETCH_SIZE", "WRITE_SIZE")}
     if other:
-        lines.append("")
-        lines.append("counter totals per kernel (summed over dispatches):")
-        for kind, sym in KERNEL_SYMBOLS.items():
+        dispatched = [(kind, sym) for kind, sym in KERNEL_SYMBOLS.items()
+                      if any(sym in r["Kernel_Name"] for rows in other.values() for r in rows)]
+        if dispatched:
+            lines.append("")
+            lines.append("counter totals per kernel (summed over dispatches):")
+        for kind, sym in dispatched:
             row = []
             for c in sorted(other):
                 v = sum(float(r["Counter_Value"]) for r in other[c] if sym in r["Kernel_Name"])
@@ -798,7 +852,9 @@ def summarize(dirs, command):
                 lines.append("")
                 lines.append("engine clock while the kernel ran (GRBM_GUI_ACTIVE / 8 / dispatch "
                              "time), GHz:")
-                for kind, sym in list(KERNEL_SYMBOLS.items()) + [("copy", "copyBuffer")]:
+                for kind, sym in list(KERNEL_SYMBOLS.items()) + [
+                        ("copy", "copyBuffer"), ("mfma_loop_constant", "mfma_loop_constant"),
+                        ("mfma_loop_random", "mfma_loop_random")]:
                     rs = [r for r in rows if sym in r["Kernel_Name"]]
                     if kind == "copy" and rs:  # the 1 GiB calibration copy only
                         rs = [max(rs, key=lambda r: int(r["End_Timestamp"]) -
@@ -840,6 +896,9 @@ def main():
     from shared_prompt_tree_amd import ops
 
     ops.library()  # fail loudly if the HIP library is missing
+    if args.mfma_ceiling:
+        print(json.dumps(mfma_ceiling(args.ceiling_seconds)), flush=True)
+        return
     if args.tile_split_sweep:
         print(json.dumps(tile_split_sweep(args.steps)), flush=True)
         return
@@ -903,6 +962,18 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    ceiling = None
+    if args.ceiling_seconds > 0:
+        # After the timed work, on the same GPU: the matrix units' sustained
+        # rate on register operands, with data like the attention operands
+        # (random) and without (constant), and each kernel's rate against
+        # the former.  The power-limited clock makes the first well below the
+        # published peak, and it varies from GPU to GPU.
+        ceiling = mfma_ceiling(args.ceiling_seconds)
+        rnd = ceiling["random"]["tflops"]
+        ceiling["kernel_frac_of_random"] = {
+            rep["config"]["workload"]: {k: round(v / rnd, 3) for k, v in rep["kernel_tflops"].items()}
+            for rep in [main_rep] + also}
     line = {
         "metric": "tree-attention fwd+bwd useful TFLOP/s per GPU",
         "value": round(main_rep["tflops"], 2),
@@ -931,6 +1002,7 @@ def main():
         "roofline": main_rep["roofline"],
         "flattened_baseline": main_rep.get("flattened_baseline"),
         "cpu_baseline": cpu,
+        "mfma_ceiling": ceiling,
         "also": also or None,
     }
     print(json.dumps(line), flush=True)

@@ -88,10 +88,12 @@ def test_engine_clock(tmp_profiles):
         return r
     _write_csv(tmp_profiles / "c" / "run_counter_collection.csv", [
         row(DKV, 8 * 2.0e6, 0, 1_000_000), row(DKV, 8 * 1.0e6, 5_000_000, 5_500_000),
-        row(COPY, 8 * 2.4e5, 0, 100_000), row(COPY, 8 * 500, 0, 100)])
+        row(COPY, 8 * 2.4e5, 0, 100_000), row(COPY, 8 * 500, 0, 100),
+        row("(anonymous namespace)::mfma_loop_random(float*)", 8 * 1.5e6, 0, 1_000_000)])
     text = bench.summarize([str(tmp_profiles / "c")], "c")
     assert "dkv: 2.000 over 2 dispatches, 1.500 ms" in text
     assert "copy: 2.400 over 1 dispatches" in text
+    assert "mfma_loop_random: 1.500 over 1 dispatches" in text
 
 
 def test_kernel_stats_table(tmp_profiles):
@@ -219,3 +221,18 @@ def test_schedule_balance_of_large_replays():
         tree = wl.make_tree(wl.SPECS[name])
         for kind in ("dq", "dkv"):
             assert 1.0 <= wl.schedule_balance(tree, kind) < 1.02, (name, kind)
+
+
+def test_mfma_ceiling_library_exports_and_checks_arguments():
+    # The measurement library builds with the others and rejects a bad
+    # argument on the host, before any HIP call (so this runs without a GPU).
+    import ctypes
+    path = os.path.join(ROOT, "shared_prompt_tree_amd", "lib", "libmfmaceiling.so")
+    assert os.path.exists(path), "build with python -m shared_prompt_tree_amd.build"
+    lib = ctypes.CDLL(path)
+    f = lib.mfma_ceiling_run
+    f.argtypes = [ctypes.c_int, ctypes.c_double, ctypes.POINTER(ctypes.c_double),
+                  ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
+    tf, first, n = ctypes.c_double(), ctypes.c_double(), ctypes.c_int()
+    assert f(1, 0.0, ctypes.byref(tf), ctypes.byref(first), ctypes.byref(n)) == -1
+    assert f(1, 1.0, None, ctypes.byref(first), ctypes.byref(n)) == -1
