@@ -864,6 +864,25 @@ def summarize(dirs, command):
                         cyc = sum(float(r["Counter_Value"]) for r in rs) / 8
                         lines.append(f"{kind}: {cyc / ns:.3f} over {len(rs)} dispatches, "
                                      f"{ns / 1e6:.3f} ms")
+        need = ("SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY")
+        if all(c in other for c in need):
+            # Per-wave time split: waiting on dependencies (waitcnt, barrier),
+            # ready but not issued (units busy with other waves), issuing.
+            def tot(c, sym):
+                return sum(float(r["Counter_Value"]) for r in other[c] if sym in r["Kernel_Name"])
+            lines.append("")
+            lines.append("share of wave time (SQ_WAVE_CYCLES): waiting on dependencies "
+                         "(SQ_WAIT_ANY), ready but not issued (SQ_WAIT_INST_ANY), issuing "
+                         "(SQ_ACTIVE_INST_ANY; with SQ_ACTIVE_INST_SCA, its scalar share):")
+            for kind, sym in dispatched:
+                w = tot("SQ_WAVE_CYCLES", sym)
+                if w <= 0:
+                    continue
+                act = tot("SQ_ACTIVE_INST_ANY", sym)
+                sca = (f" (scalar {tot('SQ_ACTIVE_INST_SCA', sym) / act:.2f} of it)"
+                       if "SQ_ACTIVE_INST_SCA" in other and act > 0 else "")
+                lines.append(f"{kind}: wait {tot('SQ_WAIT_ANY', sym) / w:.2f}, wait for issue "
+                             f"{tot('SQ_WAIT_INST_ANY', sym) / w:.2f}, issuing {act / w:.2f}{sca}")
         if "SQ_VALU_MFMA_BUSY_CYCLES" in other and "GRBM_GUI_ACTIVE" in other:
             # GRBM_GUI_ACTIVE sums the active cycles of the 8 XCDs; each of the
             # 1024 SIMDs can keep its matrix unit busy for all of them.

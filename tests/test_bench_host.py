@@ -96,6 +96,15 @@ def test_engine_clock(tmp_profiles):
     assert "mfma_loop_random: 1.500 over 1 dispatches" in text
 
 
+def test_wave_state_shares(tmp_profiles):
+    _write_csv(tmp_profiles / "s" / "run_counter_collection.csv", [
+        _ctr(DKV, "SQ_WAVE_CYCLES", 1000), _ctr(DKV, "SQ_WAIT_ANY", 400),
+        _ctr(DKV, "SQ_WAIT_INST_ANY", 250), _ctr(DKV, "SQ_ACTIVE_INST_ANY", 350),
+        _ctr(DKV, "SQ_ACTIVE_INST_SCA", 70)])
+    text = bench.summarize([str(tmp_profiles / "s")], "c")
+    assert "dkv: wait 0.40, wait for issue 0.25, issuing 0.35 (scalar 0.20 of it)" in text
+
+
 def test_kernel_stats_table(tmp_profiles):
     _write_csv(tmp_profiles / "k" / "run_kernel_stats.csv", [
         {"Name": DKV, "Calls": "4", "AverageNs": "2500000", "TotalDurationNs": "10000000",
