@@ -16,8 +16,10 @@ Prints one JSON line.  Besides the headline numbers it carries:
   breakdown_ms       time per entry point (HIP events between the calls)
   roofline           the dominant kernel's own duration (HIP events recorded
                      by the library around that kernel) against the bf16
-                     MFMA peak; per launch, its measured HBM bytes, the
-                     algorithmic bytes and the achieved HBM bandwidth
+                     MFMA peak (and, as frac_of_measured_ceiling, against
+                     the random-operand rate of mfma_ceiling below); per
+                     launch, its measured HBM bytes, the algorithmic bytes
+                     and the achieved HBM bandwidth
   flattened_baseline the same attention computed the way flattened context
                      parallelism does it: every (prompt, response) pair as
                      its own causal sequence, with the same kernels
@@ -993,6 +995,10 @@ def main():
         ceiling["kernel_frac_of_random"] = {
             rep["config"]["workload"]: {k: round(v / rnd, 3) for k, v in rep["kernel_tflops"].items()}
             for rep in [main_rep] + also}
+        for rep in [main_rep] + also:
+            # the dominant kernel against what this GPU sustains on such data
+            rep["roofline"]["frac_of_measured_ceiling"] = round(
+                rep["roofline"]["achieved"] / rnd, 4)
     line = {
         "metric": "tree-attention fwd+bwd useful TFLOP/s per GPU",
         "value": round(main_rep["tflops"], 2),
