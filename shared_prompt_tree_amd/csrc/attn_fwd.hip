@@ -22,6 +22,8 @@
 // transposed too, O^T += V^T P^T, with V^T read from a pre-transposed copy.
 #include <hip/hip_ext.h>
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -96,10 +98,10 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs<T, D> a) {
   const int total = na + nb;
   const size_t kv_stride = (size_t)a.hkv * D;
 
-  // Tile j into LDS stage j % NSTAGE: K rows (keys past the segment are
+  // Tile j into LDS stage `stage`: K rows (keys past the segment are
   // clamped to its last key and masked later) and V^T rows (padded copy,
   // always in range).
-  auto gload = [&](int j) {
+  auto gload = [&](int j, int stage) {
     const bool inA = j < na;
     const int ks = (inA ? j : j - na) * KT;
     const T* kbase = (inA ? a.k_a + (size_t)it.a0 * kv_stride : a.k_b + (size_t)it.b0 * kv_stride) +
@@ -108,7 +110,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs<T, D> a) {
     const int vstride = inA ? a.vt_a_stride : a.vt_b_stride;
     const T* vbase = inA ? a.vt_a + (size_t)kv * D * a.vt_a_stride + it.apad + ks
                          : a.vt_b + (size_t)kv * D * a.vt_b_stride + it.bpad + ks;
-    T* kt = smem + (j % NSTAGE) * STAGE;
+    T* kt = smem + stage * STAGE;
     g2l_tile<T, KT, NCHK, NT>(kt, kbase, [&](int r) { return min(r, klast) * (int)kv_stride; });
     g2l_tile<T, D, NCHV, NT>(kt + KTILE, vbase, [&](int r) { return r * vstride; });
   };
@@ -135,116 +137,131 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs<T, D> a) {
     // triple buffered.  After the first half of tile j every wave waits for
     // its copies of tile j + 1 and meets the others at one barrier; by then
     // tile j - 1 is no longer read, and tile j + 2 is copied into its stage.
-    const int nhalf = 2 * total;
-    if (total > 0) gload(0);
-    if (total > 1) gload(1);
+    // Tiles rotate through the stages (tile j in stage j % NSTAGE, kept as
+    // a counter), and the two halves of a tile are separate instances of
+    // the loop body, so that the half index and everything derived from it
+    // are compile-time constants.
+    if (total > 0) gload(0, 0);
+    if (total > 1) gload(1, 1);
     wait_vmem();
     __syncthreads();
     f32x16 s_cur = f32x16{}, s_nxt = f32x16{};
     Frag<T> kf[2];
-    auto kload = [&](int hh, int kk, int slot) {
-      const T* kt = smem + ((hh >> 1) % NSTAGE) * STAGE;
-      lds_frag(kf[slot], kt, 32 * (hh & 1) + lr, KROW, 16 * kk + 8 * lh);
+    auto kload = [&](const T* kt, int row0, int kk, int slot) {
+      lds_frag(kf[slot], kt, row0 + lr, KROW, 16 * kk + 8 * lh);
     };
-    if (nhalf > 0) {
-      kload(0, 0, 0);
+    if (total > 0) {
+      kload(smem, 0, 0, 0);
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        if (kk + 1 < NKK) kload(0, kk + 1, (kk + 1) & 1);
+        if (kk + 1 < NKK) kload(smem, 0, kk + 1, (kk + 1) & 1);
         mma(s_cur, kf[kk & 1], qf[kk]);
       }
     }
-    for (int h = 0; h < nhalf; ++h) {
-      const int j = h >> 1, e = h & 1;
-      const bool more = h + 1 < nhalf;
+    int stage = 0;  // tile j's stage
+    for (int j = 0; j < total; ++j) {
+      const int stage1 = stage == NSTAGE - 1 ? 0 : stage + 1;  // tile j + 1's
+      const T* kt = smem + stage * STAGE;
       const bool inA = j < na;
-      const int kb0 = (inA ? j : j - na) * KT + 32 * e;  // first key of the half
-      const bool need_mask = inA ? (kb0 + 32 > it.alen) : (kb0 + 31 > it.qpos + wave_tok0);
+      const int key0 = (inA ? j : j - na) * KT;  // first key of the tile
       const int lim = inA ? it.alen - 1 : it.qpos + tok;
-      s_nxt = f32x16{};
       // The next half's scores are formed unconditionally so that phase A
       // stays straight-line code; after the item's last half they come from
-      // a stage that is in bounds but stale, and are discarded.
-      const int hn = more ? h + 1 : h;
-      kload(hn, 0, 0);
-      Frag<T> pf[2];
-      float mx = -INFINITY, m_use = 0.f;
-      // phase A: scores of half h + 1 beside the softmax of half h
+      // a stage that is in bounds but stale (this tile's second half), and
+      // are discarded.
+      const bool more = j + 1 < total;
+      const T* kt_next = more ? smem + stage1 * STAGE : kt;
+      const int row_next = more ? 0 : 32;
+      auto half = [&](auto e_const) {
+        constexpr int e = decltype(e_const)::value;
+        const int kb0 = key0 + 32 * e;  // first key of the half
+        const bool need_mask = inA ? (kb0 + 32 > it.alen) : (kb0 + 31 > it.qpos + wave_tok0);
+        const T* ktn = e == 0 ? kt : kt_next;  // the next half's K
+        const int rown = e == 0 ? 32 : row_next;
+        s_nxt = f32x16{};
+        kload(ktn, rown, 0, 0);
+        Frag<T> pf[2];
+        float mx = -INFINITY, m_use = 0.f;
+        // phase A: scores of half h + 1 beside the softmax of half h
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        if (kk + 1 < NKK) kload(hn, kk + 1, (kk + 1) & 1);
-        mma(s_nxt, kf[kk & 1], qf[kk]);
-        if (kk == 0) {
-          if (need_mask) {
+        for (int kk = 0; kk < NKK; ++kk) {
+          if (kk + 1 < NKK) kload(ktn, rown, kk + 1, (kk + 1) & 1);
+          mma(s_nxt, kf[kk & 1], qf[kk]);
+          if (kk == 0) {
+            if (need_mask) {
 #pragma unroll
-            for (int jj = 0; jj < 16; ++jj) {
-              const int key = kb0 + 8 * (jj >> 2) + 4 * lh + (jj & 3);
-              if (key > lim) s_cur[jj] = -INFINITY;
+              for (int jj = 0; jj < 16; ++jj) {
+                const int key = kb0 + 8 * (jj >> 2) + 4 * lh + (jj & 3);
+                if (key > lim) s_cur[jj] = -INFINITY;
+              }
+            }
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj) mx = fmaxf(mx, s_cur[jj]);
+            mx = max_with_other_half(mx) * c2;
+          } else if (kk == 1) {
+            // lazy rescale (as in the tile loop below)
+            if (__any(mx > m_run + kRescale)) {
+              const float m_new = fmaxf(m_run, mx);
+              const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
+              lsum *= alpha;
+#pragma unroll
+              for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+              m_run = m_new;
+            }
+          } else {
+            m_use = (m_run == -INFINITY) ? 0.f : m_run;
+            constexpr int PER = 16 / (NKK - 2);  // exponentials per remaining step
+            const int base = (kk - 2) * PER;
+#pragma unroll
+            for (int u = 0; u < PER; ++u)
+              if (base + u < 16) s_cur[base + u] = fast_exp2(s_cur[base + u] * c2 - m_use);
+            if (kk == NKK - 1) {
+#pragma unroll
+              for (int jj = (NKK - 2) * PER; jj < 16; ++jj)
+                s_cur[jj] = fast_exp2(s_cur[jj] * c2 - m_use);
             }
           }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        float ps = 0.f;
 #pragma unroll
-          for (int jj = 0; jj < 16; ++jj) mx = fmaxf(mx, s_cur[jj]);
-          mx = max_with_other_half(mx) * c2;
-        } else if (kk == 1) {
-          // lazy rescale (as in the tile loop below)
-          if (__any(mx > m_run + kRescale)) {
-            const float m_new = fmaxf(m_run, mx);
-            const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
-            lsum *= alpha;
+        for (int hf = 0; hf < 2; ++hf) {
+          to_frag(pf[hf], s_cur, 8 * hf);
+          ps = frag_sum(pf[hf], ps);
+        }
+        lsum += ps;
+        // phase B: O^T += V^T P^T for half h
+        {
+          const T* vt = kt + KTILE;
+          Frag<T> vf[2];
+          auto vload = [&](int st, int slot) {  // st = 2*db + hf
+            lds_frag(vf[slot], vt, 32 * (st >> 1) + lr, VROW, 16 * (2 * e + (st & 1)) + 8 * lh);
+          };
+          vload(0, 0);
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
-            m_run = m_new;
-          }
-        } else {
-          m_use = (m_run == -INFINITY) ? 0.f : m_run;
-          constexpr int PER = 16 / (NKK - 2);  // exponentials per remaining step
-          const int base = (kk - 2) * PER;
-#pragma unroll
-          for (int u = 0; u < PER; ++u)
-            if (base + u < 16) s_cur[base + u] = fast_exp2(s_cur[base + u] * c2 - m_use);
-          if (kk == NKK - 1) {
-#pragma unroll
-            for (int jj = (NKK - 2) * PER; jj < 16; ++jj)
-              s_cur[jj] = fast_exp2(s_cur[jj] * c2 - m_use);
+          for (int st = 0; st < 2 * NDB; ++st) {
+            if (st + 1 < 2 * NDB) vload(st + 1, (st + 1) & 1);
+            mma(oacc[st >> 1], vf[st & 1], pf[st & 1]);
           }
         }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      float ps = 0.f;
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        to_frag(pf[hf], s_cur, 8 * hf);
-        ps = frag_sum(pf[hf], ps);
-      }
-      lsum += ps;
-      // phase B: O^T += V^T P^T for half h
-      {
-        const T* vt = smem + (j % NSTAGE) * STAGE + KTILE;
-        Frag<T> vf[2];
-        auto vload = [&](int st, int slot) {  // st = 2*db + hf
-          lds_frag(vf[slot], vt, 32 * (st >> 1) + lr, VROW, 16 * (2 * e + (st & 1)) + 8 * lh);
-        };
-        vload(0, 0);
-#pragma unroll
-        for (int st = 0; st < 2 * NDB; ++st) {
-          if (st + 1 < 2 * NDB) vload(st + 1, (st + 1) & 1);
-          mma(oacc[st >> 1], vf[st & 1], pf[st & 1]);
+        s_cur = s_nxt;
+        if constexpr (e == 0) {
+          // tile j + 1 complete everywhere, tile j - 1 no longer read
+          wait_vmem();
+          __syncthreads();
+          if (j + 2 < total) gload(j + 2, stage1 == NSTAGE - 1 ? 0 : stage1 + 1);
         }
-      }
-      s_cur = s_nxt;
-      if (e == 0) {
-        // tile j + 1 complete everywhere, tile j - 1 no longer read
-        wait_vmem();
-        __syncthreads();
-        if (j + 2 < total) gload(j + 2);
-      }
+      };
+      half(std::integral_constant<int, 0>{});
+      half(std::integral_constant<int, 1>{});
+      stage = stage1;
     }
   } else {
-  if (total > 0) gload(0);
+  if (total > 0) gload(0, 0);
   wait_vmem();
   __syncthreads();
   for (int j = 0; j < total; ++j) {
-    if (j + 1 < total) gload(j + 1);
+    if (j + 1 < total) gload(j + 1, (j + 1) & 1);
     const T* kt = smem + (j & 1) * STAGE;
     const T* vt = kt + KTILE;
 
