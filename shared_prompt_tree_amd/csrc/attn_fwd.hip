@@ -98,21 +98,43 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs<T, D> a) {
   const int total = na + nb;
   const size_t kv_stride = (size_t)a.hkv * D;
 
-  // Tile j into LDS stage `stage`: K rows (keys past the segment are
+  // Tiles are copied in order (j = 0, 1, ...), segment A's then B's; a
+  // copy cursor holds the next tile's K and V^T bases, the rows left in its
+  // segment and the V^T row stride, and advances by one tile per copy.
+  const T* kcur;
+  const T* vcur;
+  int klast, vstride;
+  auto cursor_to_b = [&]() {
+    kcur = a.k_b + (size_t)it.b0 * kv_stride + kv * D;
+    vcur = a.vt_b + (size_t)kv * D * a.vt_b_stride + it.bpad;
+    klast = it.blen - 1;
+    vstride = a.vt_b_stride;
+  };
+  if (na > 0) {
+    kcur = a.k_a + (size_t)it.a0 * kv_stride + kv * D;
+    vcur = a.vt_a + (size_t)kv * D * a.vt_a_stride + it.apad;
+    klast = it.alen - 1;
+    vstride = a.vt_a_stride;
+  } else {
+    cursor_to_b();
+  }
+  int copied = 0;
+  // The next tile into LDS stage `stage`: K rows (keys past the segment are
   // clamped to its last key and masked later) and V^T rows (padded copy,
   // always in range).
-  auto gload = [&](int j, int stage) {
-    const bool inA = j < na;
-    const int ks = (inA ? j : j - na) * KT;
-    const T* kbase = (inA ? a.k_a + (size_t)it.a0 * kv_stride : a.k_b + (size_t)it.b0 * kv_stride) +
-                     (size_t)ks * kv_stride + kv * D;
-    const int klast = (inA ? it.alen : it.blen) - 1 - ks;
-    const int vstride = inA ? a.vt_a_stride : a.vt_b_stride;
-    const T* vbase = inA ? a.vt_a + (size_t)kv * D * a.vt_a_stride + it.apad + ks
-                         : a.vt_b + (size_t)kv * D * a.vt_b_stride + it.bpad + ks;
+  auto gload_next = [&](int stage) {
     T* kt = smem + stage * STAGE;
-    g2l_tile<T, KT, NCHK, NT>(kt, kbase, [&](int r) { return min(r, klast) * (int)kv_stride; });
-    g2l_tile<T, D, NCHV, NT>(kt + KTILE, vbase, [&](int r) { return r * vstride; });
+    const int kl = klast;
+    g2l_tile<T, KT, NCHK, NT>(kt, kcur, [&](int r) { return min(r, kl) * (int)kv_stride; });
+    const int vs = vstride;
+    g2l_tile<T, D, NCHV, NT>(kt + KTILE, vcur, [&](int r) { return r * vs; });
+    if (++copied == na) {
+      cursor_to_b();
+    } else {
+      kcur += (size_t)KT * kv_stride;
+      vcur += KT;
+      klast -= KT;
+    }
   };
 
   f32x16 oacc[NDB];
@@ -141,8 +163,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs<T, D> a) {
     // a counter), and the two halves of a tile are separate instances of
     // the loop body, so that the half index and everything derived from it
     // are compile-time constants.
-    if (total > 0) gload(0, 0);
-    if (total > 1) gload(1, 1);
+    if (total > 0) gload_next(0);
+    if (total > 1) gload_next(1);
     wait_vmem();
     __syncthreads();
     f32x16 s_cur = f32x16{}, s_nxt = f32x16{};
@@ -249,7 +271,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs<T, D> a) {
           // tile j + 1 complete everywhere, tile j - 1 no longer read
           wait_vmem();
           __syncthreads();
-          if (j + 2 < total) gload(j + 2, stage1 == NSTAGE - 1 ? 0 : stage1 + 1);
+          if (j + 2 < total) gload_next(stage1 == NSTAGE - 1 ? 0 : stage1 + 1);
         }
       };
       half(std::integral_constant<int, 0>{});
@@ -257,11 +279,11 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs<T, D> a) {
       stage = stage1;
     }
   } else {
-  if (total > 0) gload(0, 0);
+  if (total > 0) gload_next(0);
   wait_vmem();
   __syncthreads();
   for (int j = 0; j < total; ++j) {
-    if (j + 1 < total) gload(j + 1, (j + 1) & 1);
+    if (j + 1 < total) gload_next((j + 1) & 1);
     const T* kt = smem + (j & 1) * STAGE;
     const T* vt = kt + KTILE;
 
