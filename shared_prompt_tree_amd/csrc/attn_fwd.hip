@@ -99,8 +99,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs<T, D> a) {
   const size_t kv_stride = (size_t)a.hkv * D;
 
   // Tiles are copied in order (j = 0, 1, ...), segment A's then B's; a
-  // copy cursor holds the next tile's K and V^T bases, the rows left in its
-  // segment and the V^T row stride, and advances by one tile per copy.
+  // copy cursor holds the next tile's K and V^T bases, its segment's last
+  // key counted from the tile's first (K rows past it are clamped to it) and
+  // the V^T row stride, and advances by one tile per copy.
   const T* kcur;
   const T* vcur;
   int klast, vstride;
