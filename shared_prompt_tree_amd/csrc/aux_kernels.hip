@@ -348,7 +348,12 @@ hipError_t launch_seed_reduce(const SeedReduceArgs& a, hipStream_t s) {
 //
 // out[hg][d][perm(col)] for 64 columns per workgroup.  Column col of head
 // group hg is token u = (col - pad[s]*hp) / hp of segment s and head
-// hg*hp + col % hp; padding columns are written as zeros.
+// hg*hp + col % hp; padding columns are written as zeros.  Optionally (the
+// dO copy of the backward) the same pass forms the row dot
+// delta[h][t] = sum_c dO[t][h][c] O[t][h][c] in float32: each thread also
+// loads the O chunk of its dO chunk, and the nch lanes that hold one column
+// (a power of two, consecutive within a wave) add their partial sums by
+// shuffles.
 
 template <typename T>
 __global__ __launch_bounds__(kAuxThreads) void transpose_kernel(TransposeArgs a) {
@@ -359,6 +364,7 @@ __global__ __launch_bounds__(kAuxThreads) void transpose_kernel(TransposeArgs a)
   const int hg = blockIdx.y;
   const int hp = a.hp;
   const T* in = static_cast<const T*>(a.in);
+  const T* with = static_cast<const T*>(a.dot_with);
   T* out = static_cast<T*>(a.out);
   constexpr int CH = 16 / sizeof(T);
   const int nch = a.d / CH;
@@ -377,14 +383,29 @@ __global__ __launch_bounds__(kAuxThreads) void transpose_kernel(TransposeArgs a)
     const int s = lo;
     const int seg_len = a.seg_cu[s + 1] - a.seg_cu[s];
     const int u0 = (int)((col0 - (long long)a.seg_pad[s] * hp) / hp);
+    // C * nch is a multiple of kAuxThreads, so every thread runs every
+    // iteration (the shuffles below need all lanes)
     for (int q = threadIdx.x; q < C * nch; q += kAuxThreads) {
       const int c = q / nch, ch = q % nch;
       const int u = u0 + c / hp;
+      const size_t off =
+          ((size_t)(a.seg_cu[s] + (u < seg_len ? u : 0)) * a.heads + hg * hp + c % hp) * a.d +
+          ch * CH;
       u32x4 v = u32x4{0, 0, 0, 0};
-      if (u < seg_len)
-        v = *reinterpret_cast<const u32x4*>(
-            in + ((size_t)(a.seg_cu[s] + u) * a.heads + hg * hp + c % hp) * a.d + ch * CH);
+      if (u < seg_len) v = *reinterpret_cast<const u32x4*>(in + off);
       *reinterpret_cast<u32x4*>(tile + c * ld + ch * CH) = v;
+      if (with != nullptr) {
+        u32x4 wv = u32x4{0, 0, 0, 0};
+        if (u < seg_len) wv = *reinterpret_cast<const u32x4*>(with + off);
+        const T* x = reinterpret_cast<const T*>(&v);
+        const T* y = reinterpret_cast<const T*>(&wv);
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < CH; ++e) acc += to_f32(x[e]) * to_f32(y[e]);
+        for (int o = nch >> 1; o > 0; o >>= 1) acc += __shfl_xor(acc, o, nch);
+        if (ch == 0 && u < seg_len)
+          a.dot_out[(size_t)(hg * hp + c % hp) * a.dot_tokens + a.seg_cu[s] + u] = acc;
+      }
     }
     __syncthreads();
     for (int q = threadIdx.x; q < a.d * (C / CH); q += kAuxThreads) {
@@ -413,56 +434,6 @@ hipError_t launch_transpose(const TransposeArgs& a, int dtype, hipStream_t s) {
   const size_t smem = 64 * (size_t)(a.d + 8) * esz;
   if (dtype == 1) hipLaunchKernelGGL(transpose_kernel<bf16>, grid, dim3(kAuxThreads), smem, s, a);
   else hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(kAuxThreads), smem, s, a);
-  return hipGetLastError();
-}
-
-// ------------------------------------------------------------ row dot
-// delta[h][t] = sum_c dout[t][h][c] * out[t][h][c]; 16 lanes per row.
-
-template <typename T>
-__global__ __launch_bounds__(kAuxThreads) void row_dot_kernel(const T* dout, const T* out,
-                                                              float* delta, int tokens, int heads,
-                                                              int d) {
-  constexpr int CH = 16 / sizeof(T);
-  const int lanes = d / CH;  // 16 (bf16, d=128) ... 4 (fp32, d=64)... per row
-  const long long rows = (long long)tokens * heads;
-  // 16 consecutive threads per row; the stride is a multiple of 16, so the
-  // 16 lanes of a row stay together (and leave the loop together)
-  for (long long gid = aux_first(blockIdx.x, threadIdx.x); gid < rows * 16;
-       gid += aux_stride(gridDim.x)) {
-    const long long row = gid / 16;
-    const int part = (int)(gid % 16);
-    float acc = 0.f;
-    const size_t base = (size_t)row * d;
-    for (int ch = part; ch < lanes; ch += 16) {
-      T x[CH], y[CH];
-      *reinterpret_cast<u32x4*>(x) = *reinterpret_cast<const u32x4*>(dout + base + ch * CH);
-      *reinterpret_cast<u32x4*>(y) = *reinterpret_cast<const u32x4*>(out + base + ch * CH);
-#pragma unroll
-      for (int e = 0; e < CH; ++e) acc += to_f32(x[e]) * to_f32(y[e]);
-    }
-#pragma unroll
-    for (int off = 8; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 16);
-    if (part == 0) {
-      const long long t = row / heads, h = row % heads;
-      delta[h * tokens + t] = acc;
-    }
-  }
-}
-
-hipError_t launch_row_dot(const void* dout, const void* out, float* delta, int tokens, int heads,
-                          int d, int dtype, hipStream_t s) {
-  const long long rows = (long long)tokens * heads;
-  if (rows == 0) return hipSuccess;
-  const int grid = (int)aux_blocks(rows * 16);
-  if (dtype == 1)
-    hipLaunchKernelGGL(row_dot_kernel<bf16>, dim3(grid), dim3(kAuxThreads), 0, s,
-                       static_cast<const bf16*>(dout), static_cast<const bf16*>(out), delta,
-                       tokens, heads, d);
-  else
-    hipLaunchKernelGGL(row_dot_kernel<float>, dim3(grid), dim3(kAuxThreads), 0, s,
-                       static_cast<const float*>(dout), static_cast<const float*>(out), delta,
-                       tokens, heads, d);
   return hipGetLastError();
 }
 

@@ -82,12 +82,15 @@ struct TransposeArgs {
   const int32_t* seg_cu;
   const int32_t* seg_pad;
   int pad_tokens;  // seg_pad[n_seg], from the host
+  // Optional (both null: off): while copying `in` (dO), also the backward's
+  // row dot delta[h][t] = sum_c in[t][h][c] * dot_with[t][h][c] in float32,
+  // delta row stride dot_tokens (the tensor's tokens).
+  const void* dot_with = nullptr;
+  float* dot_out = nullptr;
+  int dot_tokens = 0;
 };
 hipError_t launch_transpose(const TransposeArgs& a, int dtype, hipStream_t s);
 
-// delta[h][t] = sum_c dout[t][h][c] * out[t][h][c] in float32.
-hipError_t launch_row_dot(const void* dout, const void* out, float* delta, int tokens, int heads,
-                          int d, int dtype, hipStream_t s);
 
 hipError_t launch_lse_merge(int splits, int rows, int heads, int d, int out_dtype,
                             const float* o_parts, const float* lse_parts, void* o_out,

@@ -5,11 +5,12 @@
 //   prefill      : work list, V^T copy, forward kernel
 //   replay_fwd   : work list, V^T copies, forward kernel (prompt column and
 //                  own branch merged in one online-softmax state)
-//   replay_bwd   : delta, work lists, K^T / Q^T / dO^T copies, dQ kernel,
-//                  dK/dV kernel (prompt tiles write float32 seeds summed over
-//                  every branch; own-branch tiles write dK_R, dV_R)
-//   prefill_bwd  : delta, work lists, K^T / Q^T / dO^T copies, dQ kernel,
-//                  dK/dV kernel (prefill term plus the seeds)
+//   replay_bwd   : work lists, K^T / Q^T / dO^T copies (the dO^T copy also
+//                  forms delta = rowsum(dO o O)), dQ kernel, dK/dV kernel
+//                  (prompt tiles write float32 seeds summed over every
+//                  branch; own-branch tiles write dK_R, dV_R)
+//   prefill_bwd  : work lists, K^T / Q^T / dO^T copies (with delta), dQ
+//                  kernel, dK/dV kernel (prefill term plus the seeds)
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -479,10 +480,16 @@ hipError_t run_meta(const tree_attn_problem* p, const Shape& s, const MetaBufs& 
   return launch_meta(a, st);
 }
 
+// Transposed padded copy of `in`; with dot_with/dot_out (the dO copy of a
+// backward call, O and delta) the same pass also forms the row dot.
 hipError_t run_transpose(const void* in, void* out, int heads, int hp, const Shape& s, int n_seg,
                          const int32_t* seg_cu_d, const int32_t* seg_pad_d, long long pad_tokens,
-                         hipStream_t st) {
+                         hipStream_t st, const void* dot_with = nullptr, float* dot_out = nullptr,
+                         long long dot_tokens = 0) {
   TransposeArgs t;
+  t.dot_with = dot_with;
+  t.dot_out = dot_out;
+  t.dot_tokens = (int)dot_tokens;
   t.in = in;
   t.out = out;
   t.heads = heads;
@@ -736,18 +743,16 @@ int tree_attn_replay_bwd(const tree_attn_problem* problem, const void* k_p, cons
   if (fused) {
     // dQ from the dK/dV kernel: only the transposed Q and dO copies and the
     // zeroed float32 accumulator are needed
-    TA_TRY(launch_row_dot(do_r, o_r, pl.delta, (int)s.r_tokens, s.hq, s.d, s.dtype, st));
     TA_TRY(run_transpose(q_r, pl.qt, s.hq, s.hp, s, s.nb, problem->resp_cu_d, pl.mk.resp_pad,
                          s.r_pad, st));
     TA_TRY(run_transpose(do_r, pl.dot, s.hq, s.hp, s, s.nb, problem->resp_cu_d, pl.mk.resp_pad,
-                         s.r_pad, st));
+                         s.r_pad, st, o_r, pl.delta, s.r_tokens));
     TA_TRY(launch_zero(pl.dq_acc, s.r_tokens * s.hq * s.d, st));
   } else if (!s.fused_replay) {  // (fused with no response row: nothing to do for dQ)
     TA_TRY(run_meta(problem, s, pl.mq, kMetaQReplay, s.q_items_replay * s.col_splits_bwd, st, 0,
                     s.col_splits_bwd));
   }
   if (s.r_tokens > 0 && !fused) {
-    TA_TRY(launch_row_dot(do_r, o_r, pl.delta, (int)s.r_tokens, s.hq, s.d, s.dtype, st));
     TA_TRY(run_transpose(k_p, pl.kt_p, s.hkv, 1, s, s.ng, problem->prompt_cu_d,
                          pl.mq.prompt_pad, s.p_pad, st));
     TA_TRY(run_transpose(k_r, pl.kt_r, s.hkv, 1, s, s.nb, problem->resp_cu_d, pl.mq.resp_pad,
@@ -755,7 +760,7 @@ int tree_attn_replay_bwd(const tree_attn_problem* problem, const void* k_p, cons
     TA_TRY(run_transpose(q_r, pl.qt, s.hq, s.hp, s, s.nb, problem->resp_cu_d, pl.mq.resp_pad,
                          s.r_pad, st));
     TA_TRY(run_transpose(do_r, pl.dot, s.hq, s.hp, s, s.nb, problem->resp_cu_d, pl.mq.resp_pad,
-                         s.r_pad, st));
+                         s.r_pad, st, o_r, pl.delta, s.r_tokens));
     DqLaunch q;
     q.q = q_r;
     q.dout = do_r;
@@ -862,14 +867,13 @@ int tree_attn_prefill_bwd(const tree_attn_problem* problem, const void* q_p, con
   TA_TRY(run_meta(problem, s, pl.mk, kMetaKPrefill, s.k_items_prefill, st));
   const bool fused = s.fused_prefill;
   if (!fused) TA_TRY(run_meta(problem, s, pl.mq, kMetaQPrefill, s.q_items_prefill, st));
-  TA_TRY(launch_row_dot(do_p, o_p, pl.delta, (int)s.p_tokens, s.hq, s.d, s.dtype, st));
   if (!fused)
     TA_TRY(run_transpose(k_p, pl.kt_p, s.hkv, 1, s, s.ng, problem->prompt_cu_d, pl.mk.prompt_pad,
                          s.p_pad, st));
   TA_TRY(run_transpose(q_p, pl.qt, s.hq, s.hp, s, s.ng, problem->prompt_cu_d, pl.mk.prompt_pad,
                        s.p_pad, st));
   TA_TRY(run_transpose(do_p, pl.dot, s.hq, s.hp, s, s.ng, problem->prompt_cu_d,
-                       pl.mk.prompt_pad, s.p_pad, st));
+                       pl.mk.prompt_pad, s.p_pad, st, o_p, pl.delta, s.p_tokens));
   if (fused) TA_TRY(launch_zero(pl.dq_acc, s.p_tokens * s.hq * s.d, st));
   DqLaunch q;
   q.q = q_p;
